@@ -1,0 +1,56 @@
+"""Acceptance check of a GPU result against the oracle.  TEST INFRASTRUCTURE ONLY.
+
+Every element must satisfy
+
+    |C_gpu - C_ref| <= 2 * K * 2**-24 * S + ulp_out(C_ref)
+
+where C_ref and S = sum_k |A||B| (scales included) come from the oracle in
+binary64.  2*K*2**-24*S bounds the error of any fp32 accumulation order of K
+exact products (each partial sum rounds with relative error <= 2**-24, and
+the sum of |partial sums| is at most K*S; the factor 2 leaves room for the
+inner order of the matrix instructions).  ulp_out is one unit in the last
+place of the output type at C_ref (0 for fp32 output), covering the final
+round-to-nearest conversion.  NaN or Inf in the GPU result always fails.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_U24 = 2.0 ** -24
+
+
+def ulp_out(cref: np.ndarray, out_dtype: str) -> np.ndarray:
+    """One output ulp at |C_ref|: bf16 2^(e-7) with e >= -126; fp16 2^(e-10) with e >= -14."""
+    if out_dtype == "f32":
+        return np.zeros_like(cref)
+    a = np.abs(cref)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    if out_dtype == "bf16":
+        e = np.where(a > 0, np.maximum(e, -126.0), -126.0)
+        return np.exp2(e - 7.0)
+    if out_dtype == "f16":
+        e = np.where(a > 0, np.maximum(e, -14.0), -14.0)
+        return np.exp2(e - 10.0)
+    raise ValueError(out_dtype)
+
+
+def tolerance(S: np.ndarray, cref: np.ndarray, K: int, out_dtype: str) -> np.ndarray:
+    return 2.0 * K * _U24 * S + ulp_out(cref, out_dtype)
+
+
+def check(c_gpu: np.ndarray, cref: np.ndarray, S: np.ndarray, K: int, out_dtype: str):
+    """Return (ok, max_ratio, worst_index); ratio = |err| / tol (0/0 counts as 0)."""
+    c_gpu = np.asarray(c_gpu, dtype=np.float64)
+    assert c_gpu.shape == cref.shape == S.shape, (c_gpu.shape, cref.shape, S.shape)
+    if c_gpu.size == 0:
+        return True, 0.0, None
+    finite = np.isfinite(c_gpu)
+    err = np.abs(c_gpu - cref)
+    tol = tolerance(S, cref, K, out_dtype)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(err == 0, 0.0, err / tol)
+    ratio = np.where(finite, ratio, np.inf)
+    idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    mx = float(ratio[idx])
+    return bool(mx <= 1.0), mx, tuple(int(i) for i in idx)

@@ -1,0 +1,358 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each pin is chosen so that a plausible mistake in the oracle (a dropped term,
+a wrong sign or index, a transposed operand, a double rounding, a wrong nibble
+or group index) fails at least one of them:
+
+* codecs: exhaustive against numpy / torch casts (library routines);
+* GEMM: hand-worked products (tests/golden), closed forms (all-ones, identity,
+  permutation), transposition and storage-layout invariances, exact rational
+  brute force on tiny inputs, bit-identity of the threaded loop with the naive
+  triple loop;
+* int4 dequant: hand-worked words and a worked rounding case (tests/golden),
+  exhaustive over every positive finite fp16 scale against numpy's correctly
+  rounded binary64 -> binary16 conversion, a closed form for the group index.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import check as ochk
+import synth
+from _golden import load_dequant_cases, load_matrices
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+FMT_TORCH = {oracle.F16: torch.float16, oracle.BF16: torch.bfloat16, oracle.E4M3: torch.float8_e4m3fn}
+
+
+def _to_fmt(x, fmt):
+    return torch.as_tensor(np.asarray(x, dtype=np.float32)).to(FMT_TORCH[fmt])
+
+
+# ----------------------------------------------------------------- codecs
+
+def test_decode_f16_exhaustive():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode(oracle.F16, bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_decode_bf16_exhaustive():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode(oracle.BF16, bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_decode_e4m3_exhaustive():
+    bits = np.arange(256, dtype=np.uint8)
+    got = oracle.decode(oracle.E4M3, bits)
+    ref = torch.from_numpy(bits.copy()).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2  # 0x7F and 0xFF
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def _f16_neighbourhood():
+    """Doubles at and next to every fp16 rounding midpoint, plus wide random values."""
+    pos = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    mids = (pos[:-1] + pos[1:]) / 2.0  # exact in binary64
+    xs = [pos, mids, np.nextafter(mids, 0.0), np.nextafter(mids, np.inf),
+          np.array([65504.0, 65519.99, 65520.0, 65536.0, 1e6, 2.0 ** -25, 2.0 ** -26, 3 * 2.0 ** -26])]
+    rng = np.random.default_rng(123)
+    xs.append(rng.standard_normal(20000) * np.exp2(rng.integers(-30, 18, 20000)))
+    x = np.concatenate(xs)
+    return np.concatenate([x, -x])
+
+
+def test_encode_f16_matches_numpy():
+    x = _f16_neighbourhood()
+    got = oracle.encode_f16(x)
+    ref = x.astype(np.float16).view(np.uint16)  # numpy rounds binary64 -> binary16 directly
+    assert np.array_equal(got, ref)
+
+
+def _bf16_rne_fraction(x: float) -> float:
+    """Textbook RNE to bfloat16 (8 significand bits) with exact rationals."""
+    if x == 0:
+        return 0.0
+    a = Fraction(abs(x))
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)
+    q = Fraction(2) ** (e - 7)
+    n = a / q
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = float(fl * q)
+    return -v if x < 0 else v
+
+
+def test_encode_bf16_exact_rational():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(3000) * np.exp2(rng.integers(-140, 120, 3000))
+    # double-rounding traps: just above a bf16 midpoint but below it after a first rounding to fp32
+    base = np.array([1.0, 1.5, 3.0, 2.0 ** -120, 2.0 ** 100])
+    traps = base * (1 + 2.0 ** -8 + 2.0 ** -30)
+    x = np.concatenate([x, traps, -traps, base * (1 + 2.0 ** -8)])
+    got = oracle.decode(oracle.BF16, oracle.encode_bf16(x))
+    ref = np.array([_bf16_rne_fraction(float(v)) for v in x])
+    assert np.array_equal(got, ref)
+    # the trap values differ from the via-fp32 rounding
+    via32 = torch.from_numpy(traps.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert not np.array_equal(oracle.decode(oracle.BF16, oracle.encode_bf16(traps)), via32)
+
+
+def test_encode_bf16_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(8)
+    x32 = (rng.standard_normal(50000) * np.exp2(rng.integers(-100, 100, 50000))).astype(np.float32)
+    got = oracle.encode_bf16(x32.astype(np.float64))
+    ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_generator_spot_values():
+    """The input generator's e4m3 cast: ties to even near zero, saturation handled by the clamp."""
+    t = torch.tensor([2.0 ** -10, 3 * 2.0 ** -10, 449.0, 464.0]).to(torch.float8_e4m3fn).double()
+    assert t.tolist() == [0.0, 2.0 ** -8, 448.0, 448.0]
+    q, s = synth.quantize_e4m3(torch.tensor([[500.0, -1000.0, 0.5]]))
+    assert s == pytest.approx(1000.0 / 448.0)
+    assert not torch.isnan(q.double()).any()
+    assert q.double()[0, 1] == -448.0
+
+
+# ------------------------------------------------------------------ GEMM
+
+@pytest.mark.parametrize("name", ["gemm_2x2x2.txt", "gemm_2x3x2.txt"])
+@pytest.mark.parametrize("fmt", [oracle.F16, oracle.BF16, oracle.E4M3, oracle.F64])
+def test_golden_products(name, fmt):
+    g = load_matrices(name)
+    A, B, C = g["A"], g["B"], g["C"]
+    if fmt == oracle.F64:
+        a, b_kn, b_nk = A, B, np.ascontiguousarray(B.T)
+    else:
+        a, b_kn, b_nk = _to_fmt(A, fmt), _to_fmt(B, fmt), _to_fmt(B.T.copy(), fmt)
+    for b, lay in ((b_kn, oracle.B_KN), (b_nk, oracle.B_NK)):
+        got, S = oracle.gemm(fmt, a, b, lay)
+        assert np.array_equal(got, C)
+        assert np.array_equal(S, C)  # all inputs positive
+        got_n, _ = oracle.gemm(fmt, a, b, lay, naive=True)
+        assert np.array_equal(got_n, C)
+
+
+def test_planted_transpose_is_caught():
+    """A transposed B (the layout flag taken the wrong way) fails the 2x3x2 golden."""
+    g = load_matrices("gemm_2x3x2.txt")
+    b_sq = g["B"][:2, :]  # 2x2 so both readings are shape-valid
+    a_sq = g["A"][:, :2]
+    right, _ = oracle.gemm(oracle.F64, a_sq, b_sq, oracle.B_KN)
+    wrong, _ = oracle.gemm(oracle.F64, a_sq, b_sq, oracle.B_NK)
+    assert np.array_equal(right, a_sq @ b_sq)
+    assert not np.array_equal(right, wrong)
+
+
+def test_output_rounding_example():
+    g = load_matrices("gemm_round_fp32.txt")
+    a = _to_fmt(g["A"], oracle.BF16)
+    b = _to_fmt(g["B"], oracle.BF16)
+    C, _ = oracle.gemm(oracle.BF16, a, b, oracle.B_KN)
+    assert C[0, 0] == g["C"][0, 0] == 16777217.0
+    assert float(np.float32(C[0, 0])) == g["C_fp32"][0, 0]
+
+
+@pytest.mark.parametrize("fmt", [oracle.F16, oracle.BF16, oracle.E4M3])
+@pytest.mark.parametrize("K", [1, 7, 64, 300])
+def test_all_ones_closed_form(fmt, K):
+    M, N = 5, 9
+    a = _to_fmt(np.ones((M, K)), fmt)
+    b = _to_fmt(np.ones((N, K)), fmt)
+    C, S = oracle.gemm(fmt, a, b, oracle.B_NK)
+    assert np.all(C == K) and np.all(S == K)
+
+
+@pytest.mark.parametrize("fmt", [oracle.F16, oracle.BF16, oracle.E4M3])
+def test_identity_and_permutation(fmt):
+    rng = np.random.default_rng(3)
+    n, m = 24, 17
+    bvals = _to_fmt(rng.uniform(-2, 2, (n, m)), fmt)  # K x N, K = n
+    bdec = oracle.decode(fmt, bvals)
+    ident = _to_fmt(np.eye(n), fmt)
+    C, _ = oracle.gemm(fmt, ident, bvals, oracle.B_KN)
+    assert np.array_equal(C, bdec)
+    perm = rng.permutation(n)
+    P = np.zeros((n, n))
+    P[np.arange(n), perm] = 1.0
+    C, _ = oracle.gemm(fmt, _to_fmt(P, fmt), bvals, oracle.B_KN)
+    assert np.array_equal(C, bdec[perm])
+
+
+@pytest.mark.parametrize("fmt", [oracle.F16, oracle.BF16, oracle.E4M3])
+def test_transpose_and_layout_invariance(fmt):
+    rng = np.random.default_rng(11)
+    M, N, K = 19, 23, 41
+    a = _to_fmt(rng.standard_normal((M, K)), fmt)
+    b_nk = _to_fmt(rng.standard_normal((N, K)), fmt)
+    C, S = oracle.gemm(fmt, a, b_nk, oracle.B_NK)
+    # (A B)^T = B^T A^T: the stored N x K B used as the left operand, A as an N x K right operand
+    Ct, St = oracle.gemm(fmt, b_nk, a, oracle.B_NK)
+    assert np.array_equal(C, Ct.T) and np.array_equal(S, St.T)
+    # the same B stored K x N gives the identical C
+    b_kn = b_nk.T.contiguous()
+    C2, S2 = oracle.gemm(fmt, a, b_kn, oracle.B_KN)
+    assert np.array_equal(C, C2) and np.array_equal(S, S2)
+
+
+def _exact_product(Ad, Bd):
+    M, K = Ad.shape
+    N = Bd.shape[1]
+    out = np.empty((M, N), dtype=object)
+    for i in range(M):
+        for j in range(N):
+            out[i, j] = sum((Fraction(float(Ad[i, k])) * Fraction(float(Bd[k, j])) for k in range(K)),
+                            Fraction(0))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_fractions(seed):
+    rng = np.random.default_rng(100 + seed)
+    M, N, K = rng.integers(1, 9, 3)
+    fmt = [oracle.F16, oracle.BF16, oracle.E4M3][seed % 3]
+    a = _to_fmt(rng.uniform(-1, 1, (M, K)), fmt)
+    b = _to_fmt(rng.uniform(-1, 1, (K, N)), fmt)
+    C, S = oracle.gemm(fmt, a, b, oracle.B_KN)
+    exact = _exact_product(oracle.decode(fmt, a), oracle.decode(fmt, b))
+    for i in range(M):
+        for j in range(N):
+            err = abs(Fraction(float(C[i, j])) - exact[i, j])
+            assert err <= Fraction(int(K)) * Fraction(2) ** -53 * Fraction(float(S[i, j]))
+    # small dyadic inputs: every partial sum is representable, so the oracle is exact
+    a = _to_fmt(rng.integers(-16, 17, (M, K)) / 8.0, fmt)
+    b = _to_fmt(rng.integers(-16, 17, (K, N)) / 8.0, fmt)
+    C, _ = oracle.gemm(fmt, a, b, oracle.B_KN)
+    exact = _exact_product(oracle.decode(fmt, a), oracle.decode(fmt, b))
+    assert all(Fraction(float(C[i, j])) == exact[i, j] for i in range(M) for j in range(N))
+
+
+@pytest.mark.parametrize("fmt", [oracle.F16, oracle.BF16, oracle.E4M3])
+@pytest.mark.parametrize("lay", [oracle.B_KN, oracle.B_NK])
+def test_threaded_equals_naive(fmt, lay):
+    rng = np.random.default_rng(5)
+    M, N, K = 37, 45, 67
+    a = _to_fmt(rng.standard_normal((M, K)), fmt)
+    b = _to_fmt(rng.standard_normal((K, N) if lay == oracle.B_KN else (N, K)), fmt)
+    Cn, Sn = oracle.gemm(fmt, a, b, lay, scale_a=0.75, scale_b=1.25, naive=True)
+    for nt in (1, 3, 8):
+        C, S = oracle.gemm(fmt, a, b, lay, scale_a=0.75, scale_b=1.25, nthreads=nt)
+        assert np.array_equal(C, Cn) and np.array_equal(S, Sn)
+
+
+def test_fp8_all_ones_scaled():
+    """Ones quantise to 448 with scale 1/448, so C = K up to the fp32 scale rounding."""
+    K = 256
+    qa, sa = synth.quantize_e4m3(torch.ones(3, K))
+    qb, sb = synth.quantize_e4m3(torch.ones(4, K))
+    assert np.all(qa.double().numpy() == 448.0)
+    C, _ = oracle.gemm(oracle.E4M3, qa, qb, oracle.B_NK, scale_a=sa, scale_b=sb)
+    assert np.all(np.abs(C - K) <= K * 2.0 ** -22)
+
+
+# ---------------------------------------------------------------- dequant
+
+def test_dequant_golden_words():
+    for word, scale, zp, exp, kind in load_dequant_cases("dequant_words.txt"):
+        q = np.array([[np.int64(word).astype(np.int32) if word < 2 ** 31 else np.int32(word - 2 ** 32)]],
+                     dtype=np.int32)
+        s = np.array([[scale]], dtype=np.uint16)
+        W = oracle.dequant_w4(q, s, 8, group_size=128, zero_point=zp)
+        if kind == "bits":
+            assert W[0].tolist() == exp
+        else:
+            assert oracle.decode(oracle.F16, W[0]).tolist() == exp
+
+
+def test_planted_nibble_order_is_caught():
+    """Reading the nibbles from the high end fails the hand-worked 0x76543210 case."""
+    word, scale, zp, exp, _ = load_dequant_cases("dequant_words.txt")[0]
+    rev = int(f"{word:08x}"[::-1], 16)  # nibble order reversed
+    W = oracle.dequant_w4(np.array([[rev]], dtype=np.int64).astype(np.int32), np.array([[scale]], np.uint16), 8,
+                          zero_point=zp)
+    assert oracle.decode(oracle.F16, W[0]).tolist() != exp
+
+
+def test_dequant_exhaustive_scales():
+    """Every positive finite fp16 scale x every nibble, against numpy's single rounding."""
+    scales = np.arange(1, 0x7C00, dtype=np.uint16)  # 31743 columns
+    N, K = scales.size, 128
+    words = np.full((N, K // 8), 0x76543210, dtype=np.int64)
+    words[:, 1::2] = 0xFEDCBA98
+    q = words.astype(np.uint32).view(np.int32).reshape(N, K // 8)
+    W = oracle.dequant_w4(q, scales.reshape(N, 1), K, group_size=128, zero_point=8)
+    kk = np.arange(K)
+    qv = np.where((kk // 8) % 2 == 0, kk % 8, 8 + kk % 8)
+    s64 = scales.view(np.float16).astype(np.float64)
+    ref = ((qv[None, :] - 8).astype(np.float64) * s64[:, None]).astype(np.float16).view(np.uint16)
+    assert np.array_equal(W, ref)
+
+
+def test_dequant_group_and_word_index():
+    """All nibbles 9 with zero point 8 gives W = s exactly: W[n][k] must be scales[n][k // 128]."""
+    rng = np.random.default_rng(4)
+    N, K = 6, 512
+    q = np.full((N, K // 8), 0x99999999, dtype=np.int64).astype(np.uint32).view(np.int32)
+    s = rng.uniform(0.005, 0.02, (N, K // 128)).astype(np.float16).view(np.uint16)
+    W = oracle.dequant_w4(q, s, K, group_size=128, zero_point=8)
+    assert np.array_equal(W, np.repeat(s, 128, axis=1))
+    # a distinct nibble in one word lands at k = 8*w + j only
+    q2 = np.zeros((1, 4), dtype=np.int32)
+    q2[0, 2] = 0x00F00000  # nibble 5 of word 2 -> k = 21
+    W2 = oracle.decode(oracle.F16, oracle.dequant_w4(q2, np.array([[0x3C00]], np.uint16), 32, zero_point=0))
+    assert np.nonzero(W2[0])[0].tolist() == [21] and W2[0, 21] == 15.0
+
+
+def test_w4a16_closed_form():
+    """A = ones, all nibbles 9, zero point 8: C[m][n] = 128 * sum of column n's scales."""
+    rng = np.random.default_rng(9)
+    M, N, K = 3, 5, 384
+    A = np.ones((M, K), dtype=np.float16).view(np.uint16)
+    q = np.full((N, K // 8), 0x99999999, dtype=np.int64).astype(np.uint32).view(np.int32)
+    s = rng.uniform(0.005, 0.02, (N, K // 128)).astype(np.float16)
+    C, _ = oracle.w4a16(A, q, s.view(np.uint16), K)
+    ref = 128.0 * s.astype(np.float64).sum(axis=1)
+    assert np.array_equal(C, np.broadcast_to(ref, (M, N)))
+
+
+# ---------------------------------------------------------------- checker
+
+def test_checker_bounds():
+    assert ochk.ulp_out(np.array([64.0]), "bf16")[0] == 0.5
+    assert ochk.ulp_out(np.array([1.0]), "f16")[0] == 2.0 ** -10
+    assert ochk.ulp_out(np.array([0.0]), "f16")[0] == 2.0 ** -24
+    assert ochk.ulp_out(np.array([3.0]), "f32")[0] == 0.0
+    S = np.array([[1000.0]])
+    cref = np.array([[10.0]])
+    tol = 2 * 50 * 2.0 ** -24 * 1000.0
+    ok, r, _ = ochk.check(cref + tol, cref, S, 50, "f32")
+    assert ok and r == pytest.approx(1.0)
+    ok, _, _ = ochk.check(cref + 1.01 * tol, cref, S, 50, "f32")
+    assert not ok
+    ok, r, _ = ochk.check(np.array([[np.nan]]), cref, S, 50, "f32")
+    assert not ok and r == np.inf
+    ok, _, _ = ochk.check(np.array([[np.inf]]), cref, S, 50, "bf16")
+    assert not ok
