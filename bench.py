@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the tile GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-secondary]
+
+A step is one call of the GEMM on the headline workload: bf16 4096^3, A
+row-major, B column-major, fp32 accumulate, bf16 out (inputs N(0,1) rounded
+to bf16, seeded).  One call runs the whole hot path: output-tile grid,
+global->LDS tile copies, MFMA tile products into register accumulators, the
+pipelined K loop and the epilogue store.
+
+Printed: ONE JSON line with the metric, `roofline` (the GEMM kernel's
+achieved TFLOP/s against the dense bf16 MFMA peak, from HIP events around
+each launch inside the timed region), `cpu_baseline` (the CPU oracle timed
+on a bounded sample of the same workload) and `secondary` (the skinny M=16
+GEMM's GB/s against the HBM peak, the fp8 and w4a16 workloads), each
+secondary timed launch by launch with the 256 MB Infinity Cache flushed
+before every launch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s (% MFMA peak) at bf16 4096³; GB/s (% HBM peak) at M=16 skinny"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU, dense
+PEAK_FP8_TFLOPS = 5033.2   # x 8192 FLOP/clk/CU, dense
+PEAK_HBM_GBS = 8000.0
+FLUSH_BYTES = 512 << 20   # > 2x the 256 MB Infinity Cache
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: a stored counter reading is valid only for this hash."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tile_level_gemm_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _events(n):
+    import torch
+
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def time_launches(fn, n: int, flush=None):
+    """Per-launch durations (s) from event pairs on the current stream around each call."""
+    import torch
+
+    ev = _events(n)
+    for i in range(n):
+        if flush is not None:
+            flush()
+        ev[i][0].record()
+        fn()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e-3 for a, b in ev]
+
+
+def median(xs):
+    s = sorted(xs)
+    return s[len(s) // 2]
+
+
+def make_flush():
+    import torch
+
+    buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    return lambda: buf.fill_(1.0)
+
+
+# ------------------------------------------------------------------ workloads
+
+def setup_bf16_4096():
+    import torch
+    import synth
+    import tile_level_gemm_02_amd as tg
+
+    w = synth.workload("bf16_4096")
+    A, B = w["A"].cuda(), w["B"].cuda()
+    C = torch.empty((w["M"], w["N"]), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: tg.tg_gemm_bf16(A, B, C, b_layout="col")
+    flops = 2.0 * w["M"] * w["N"] * w["K"]
+    bytes_ = 2 * (w["M"] * w["K"] + w["N"] * w["K"] + w["M"] * w["N"])
+    return w, fn, flops, bytes_
+
+
+def setup_skinny():
+    import torch
+    import synth
+    import tile_level_gemm_02_amd as tg
+
+    w = synth.workload("bf16_skinny")
+    A, B = w["A"].cuda(), w["B"].cuda()
+    C = torch.empty((w["M"], w["N"]), dtype=torch.float32, device="cuda")
+    fn = lambda: tg.tg_gemm_bf16(A, B, C, b_layout="col")
+    flops = 2.0 * w["M"] * w["N"] * w["K"]
+    bytes_ = 2 * (w["M"] * w["K"] + w["N"] * w["K"]) + 4 * w["M"] * w["N"]
+    return w, fn, flops, bytes_
+
+
+def setup_fp8():
+    import torch
+    import synth
+    import tile_level_gemm_02_amd as tg
+
+    w = synth.workload("fp8_8192")
+    A, B = w["A"].cuda(), w["B"].cuda()
+    C = torch.empty((w["M"], w["N"]), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: tg.tg_gemm_fp8(A, B, C, w["scale_a"], w["scale_b"], b_layout="col")
+    flops = 2.0 * w["M"] * w["N"] * w["K"]
+    bytes_ = w["M"] * w["K"] + w["N"] * w["K"] + 2 * w["M"] * w["N"]
+    return w, fn, flops, bytes_
+
+
+def setup_w4a16():
+    import torch
+    import synth
+    import tile_level_gemm_02_amd as tg
+
+    w = synth.workload("w4a16")
+    A, q, s = w["A"].cuda(), w["qweight"].cuda(), w["scales"].cuda()
+    C = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
+    fn = lambda: tg.tg_gemm_w4a16(A, q, s, C)
+    M, N, K = w["M"], w["N"], w["K"]
+    flops = 2.0 * M * N * K
+    bytes_ = 2 * M * K + N * K // 2 + 2 * N * (K // 128) + 2 * M * N
+    return w, fn, flops, bytes_
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(target_seconds: float = 12.0):
+    """The oracle (fp64, host threads) on a bounded row sample of the bf16 4096^3 workload."""
+    import oracle
+    import synth
+
+    w = synth.workload("bf16_4096")
+    cores = min(16, len(os.sched_getaffinity(0)))
+    # time two small row samples, fit t = t0 + rows * per_row, size the sample for ~target_seconds
+    def run(r):
+        t0 = time.perf_counter()
+        oracle.gemm(oracle.BF16, w["A"][:r], w["B"], oracle.B_NK, nthreads=cores)
+        return time.perf_counter() - t0
+
+    r1, r2 = cores, 4 * cores
+    t1, t2 = run(r1), run(r2)
+    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
+    rows2 = int(min(w["M"], max(r2, (target_seconds - max(t1 - r1 * per_row, 0.0)) / per_row)))
+    rows2 = max(cores, rows2 // cores * cores)
+    dt = run(rows2)
+    flops = 2.0 * rows2 * w["N"] * w["K"]
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows2} of {w['M']} rows of the bf16 4096^3 product (fp64 triple loop incl. "
+                      f"decode of B), {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the GEMM would shard by output columns with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    flush = make_flush()
+
+    # ---- headline: bf16 4096^3
+    w, fn, flops, nbytes = setup_bf16_4096()
+    for _ in range(args.warmup):
+        fn()
+    flush()  # inputs start the timed region in HBM, not in the Infinity Cache
+    ev = _events(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        fn()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    avg_launch = sum(per_launch) / len(per_launch)
+    ms_per_step = wall / args.steps * 1e3
+    value = flops / (wall / args.steps) / 1e12
+    achieved = flops / avg_launch / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) rounded to bf16)",
+        "config": {"workload": "bf16 GEMM M=N=K=4096, A row-major, B column-major, fp32 accumulate, bf16 out",
+                   "M": 4096, "N": 4096, "K": 4096, "b_layout": "col", "out": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": stored_traffic("bf16_4096"),
+                     "kernel": "tile_gemm<bf16, B col-major, bf16 out, 256x256>",
+                     "flop_per_launch": flops, "avg_launch_us": round(avg_launch * 1e6, 3)},
+    }
+
+    # ---- secondary workloads, each launch preceded by an Infinity Cache flush
+    if not args.no_secondary:
+        sec = {}
+        n = max(10, min(args.steps, 50))
+        for name, setup, peak_key in (("bf16_skinny", setup_skinny, "hbm"), ("fp8_8192", setup_fp8, "fp8"),
+                                      ("w4a16", setup_w4a16, "both")):
+            w2, fn2, fl2, by2 = setup()
+            for _ in range(3):
+                fn2()
+            ts = time_launches(fn2, n if name != "fp8_8192" else max(10, n // 2), flush=flush)
+            t = median(ts)
+            rec = {"median_us": round(t * 1e6, 3), "min_us": round(min(ts) * 1e6, 3),
+                   "TFLOP/s": round(fl2 / t / 1e12, 2), "GB/s": round(by2 / t / 1e9, 1),
+                   "hbm_frac": round(by2 / t / 1e9 / PEAK_HBM_GBS, 4),
+                   "algorithmic_bytes": by2, "flop": fl2}
+            if peak_key == "fp8":
+                rec["mfma_frac"] = round(fl2 / t / 1e12 / PEAK_FP8_TFLOPS, 4)
+            else:
+                rec["mfma_frac"] = round(fl2 / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+            sec[name] = rec
+            del fn2
+            torch.cuda.empty_cache()
+        out["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

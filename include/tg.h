@@ -1,0 +1,136 @@
+/*
+ * tg.h -- C ABI of the tile GEMM library for AMD MI355X (gfx950).
+ *
+ * The library computes the tile-decomposed matrix multiply C = A.B that
+ * TileLang and TileScale use as their canonical kernel, and its weight-only
+ * int4 "Dequant-GEMM" variant.  Operation, per call:
+ *
+ *     C[i][j] = alpha * sum over k of A[i][k] * B[k][j]      (fp32 accumulate)
+ *
+ * with alpha = 1 except for the fp8 entry point (alpha = scale_a * scale_b).
+ * Source of the operation: the single-GPU GEMM skeleton of "TileScale 与
+ * TileLang比较" (yaopepe.com), section 核心抽象与编程模型对比 -- an output-tile
+ * grid, shared-memory tiles of A and B, a cleared register accumulator, a
+ * pipelined loop over K that adds one tile product per step, and a final store
+ * of the accumulator.  Sizes need not divide the tile (the TileScale README's
+ * GEMM example sizes its grid with ceildiv).  The Dequant-GEMM is named as a
+ * target kernel in the same page, sections 设计目标、定位与适用场景 and
+ * 生态互操作、性能、局限与路线图.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers A, B, C, qweight, scales, W are DEVICE pointers owned by the
+ *    caller.  The library never allocates, frees or retains them and keeps no
+ *    state between calls (it is reentrant).
+ *  - Matrices are row-major with a leading dimension in ELEMENTS:
+ *      A      : M x K, element (i,k) at A[i*lda + k], lda >= K
+ *      B      : TG_ROW_MAJOR: K x N, element (k,j) at B[k*ldb + j], ldb >= N
+ *               TG_COL_MAJOR: stored N x K, element (k,j) at B[j*ldb + k], ldb >= K
+ *               (the transpose_B form; the layout of an nn.Linear weight)
+ *      C      : M x N, element (i,j) at C[i*ldc + j], ldc >= N
+ *  - C is overwritten (no beta).  M == 0 or N == 0 is a no-op returning TG_OK.
+ *    K == 0 stores zeros (an empty sum).  Any M, N, K >= 1 is handled; tails
+ *    that do not fill a tile are masked.
+ *  - Alignment: every base pointer 16-byte aligned and every leading dimension
+ *    times the element size a multiple of 16 bytes; else TG_ERR_MISALIGNED.
+ *  - C must not overlap A or B (not checked).
+ *  - Execution is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  No call synchronizes.  Argument validation is synchronous and
+ *    happens before any HIP call: an invalid call launches nothing.  A failed
+ *    launch returns TG_ERR_LAUNCH.  Faults inside a kernel surface at the
+ *    caller's next synchronization.
+ *  - Sizes are int64; leading dimensions and sizes must be non-negative and
+ *    every index must fit in the addressed buffer (the caller's duty).
+ */
+#ifndef TG_H
+#define TG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TG_OK = 0,
+    TG_ERR_INVALID_VALUE = 1, /* negative size, ld too small, NULL pointer, bad enum */
+    TG_ERR_NOT_SUPPORTED = 2, /* valid request the library does not implement */
+    TG_ERR_MISALIGNED = 3,    /* base pointer or leading dimension not 16-byte aligned */
+    TG_ERR_LAUNCH = 4         /* the HIP runtime refused the launch */
+} tg_status;
+
+typedef enum { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 } tg_dtype;
+
+/* storage of B (a K x N operand) */
+typedef enum { TG_ROW_MAJOR = 0, TG_COL_MAJOR = 1 } tg_layout;
+
+/* fp16 x fp16 -> fp32 accumulate -> C of c_dtype (TG_F32, TG_F16 or TG_BF16;
+ * conversion is round-to-nearest-even).  A, B hold IEEE binary16 elements. */
+tg_status tg_gemm_f16(int64_t M, int64_t N, int64_t K,
+                      const void *A, int64_t lda,
+                      const void *B, int64_t ldb, tg_layout b_layout,
+                      void *C, int64_t ldc, tg_dtype c_dtype,
+                      void *stream);
+
+/* bf16 x bf16 -> fp32 accumulate -> C of c_dtype.  Same contract as
+ * tg_gemm_f16 with bfloat16 inputs. */
+tg_status tg_gemm_bf16(int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda,
+                       const void *B, int64_t ldb, tg_layout b_layout,
+                       void *C, int64_t ldc, tg_dtype c_dtype,
+                       void *stream);
+
+/* fp8 (OCP e4m3, "e4m3fn": bias 7, max 448, no inf) x fp8 -> fp32
+ * accumulate; C = (scale_a * scale_b) * (Aq . Bq), converted to c_dtype.
+ * scale_a, scale_b are per-tensor dequantisation scales passed by value
+ * (finite).  Only TG_COL_MAJOR B is supported for now (else
+ * TG_ERR_NOT_SUPPORTED). */
+tg_status tg_gemm_fp8(int64_t M, int64_t N, int64_t K,
+                      const void *A, int64_t lda,
+                      const void *B, int64_t ldb, tg_layout b_layout,
+                      float scale_a, float scale_b,
+                      void *C, int64_t ldc, tg_dtype c_dtype,
+                      void *stream);
+
+/* w4a16: fp16 activations x int4 weights -> fp32 accumulate -> fp16 C.
+ *   A       : fp16 M x K row-major (lda)
+ *   qweight : int32 [N][ldq], ldq >= ceil(K/8); word w of row n packs
+ *             k = 8w .. 8w+7, nibble j (bits 4j..4j+3) holding k = 8w + j
+ *   scales  : fp16 [N][lds], lds >= ceil(K/group_size); one scale per
+ *             group of group_size consecutive k of column n
+ *   weight  : W[k][n] = fp16_RNE((q - zero_point) * scale[n][k/group_size]),
+ *             rounded once (bit-identical to tg_dequant_w4)
+ * Supported: group_size == 128, K % 128 == 0, 0 <= zero_point <= 15; other
+ * values return TG_ERR_NOT_SUPPORTED.  The int4 format is not given by the
+ * pages; this packing is the plain reading of "8 per int32 along K".
+ * Alignment: A, qweight 16 bytes; scales 2 bytes; lda*2 and ldq*4 multiples
+ * of 16; C 16 bytes with ldc*2 a multiple of 16. */
+tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K,
+                        const void *A, int64_t lda,
+                        const int32_t *qweight, int64_t ldq,
+                        const void *scales, int64_t lds,
+                        int32_t group_size, int32_t zero_point,
+                        void *C, int64_t ldc,
+                        void *stream);
+
+/* The dequant step of tg_gemm_w4a16 alone: writes W as fp16 [N][K] with
+ * leading dimension ldw (W[n*ldw + k]), using the same device routine the
+ * GEMM uses, so the two are bit-identical.  Same limits as tg_gemm_w4a16;
+ * W must be 16-byte aligned with ldw*2 a multiple of 16. */
+tg_status tg_dequant_w4(int64_t N, int64_t K,
+                        const int32_t *qweight, int64_t ldq,
+                        const void *scales, int64_t lds,
+                        int32_t group_size, int32_t zero_point,
+                        void *W, int64_t ldw,
+                        void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *tg_status_string(tg_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t tg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TG_H */

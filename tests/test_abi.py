@@ -1,0 +1,123 @@
+"""The C-ABI library: it loads, exports every declared symbol, and rejects
+invalid arguments before any HIP call (CPU only: nothing here launches)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tg.h")).read()
+    return sorted(set(re.findall(r"\b(tg_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def tg():
+    import tile_level_gemm_02_amd as tg
+
+    return tg
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared() == sorted(["tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16",
+                                  "tg_dequant_w4", "tg_status_string", "tg_version"])
+
+
+def test_library_exports_every_declared_symbol(tg):
+    lib = ctypes.CDLL(tg.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(_declared()) == set(tg.EXPORTS)
+
+
+def test_status_strings(tg):
+    for code in range(5):
+        s = tg.tg_status_string(code)
+        assert s.startswith("TG_")
+    assert "unknown" in tg.tg_status_string(99)
+    assert tg.tg_version() == 100
+
+
+A16 = 0x10000  # a fake, 16-byte aligned "device" address: never dereferenced on these paths
+
+
+def _dense(lib, fn, M=8, N=8, K=8, A=A16, lda=8, B=A16, ldb=8, lay=0, C=A16, ldc=8, cd=0):
+    return getattr(lib, fn)(M, N, K, A, lda, B, ldb, lay, C, ldc, cd, None)
+
+
+@pytest.mark.parametrize("fn", ["tg_gemm_f16", "tg_gemm_bf16"])
+def test_dense_validation(tg, fn):
+    lib = tg.lib
+    E = dict(inv=tg.TG_ERR_INVALID_VALUE, mis=tg.TG_ERR_MISALIGNED)
+    assert _dense(lib, fn, M=-1) == E["inv"]
+    assert _dense(lib, fn, K=-3) == E["inv"]
+    assert _dense(lib, fn, lay=2) == E["inv"]
+    assert _dense(lib, fn, cd=7) == E["inv"]
+    assert _dense(lib, fn, A=None) == E["inv"]
+    assert _dense(lib, fn, C=None) == E["inv"]
+    assert _dense(lib, fn, lda=7) == E["inv"]        # lda < K
+    assert _dense(lib, fn, ldc=4) == E["inv"]        # ldc < N
+    assert _dense(lib, fn, N=16, ldb=8, lay=0) == E["inv"]  # row-major B needs ldb >= N
+    assert _dense(lib, fn, K=4, lda=12) == E["mis"]  # 24 bytes per row
+    assert _dense(lib, fn, A=A16 + 8) == E["mis"]
+    assert _dense(lib, fn, C=A16 + 4) == E["mis"]
+    assert _dense(lib, fn, ldc=12, cd=1) == E["mis"]  # 24-byte fp16 rows
+    # empty problems are a successful no-op, whatever the pointers
+    assert _dense(lib, fn, M=0, A=None, B=None, C=None) == tg.TG_OK
+    assert _dense(lib, fn, N=0, A=None, B=None, C=None) == tg.TG_OK
+
+
+def test_fp8_validation(tg):
+    lib = tg.lib
+    args = lambda **k: (k.get("M", 8), 8, 8, A16, 16, A16, 16, k.get("lay", 1), k.get("sa", 1.0), 1.0,
+                        A16, 8, 0, None)
+    assert lib.tg_gemm_fp8(*args(M=-1)) == tg.TG_ERR_INVALID_VALUE
+    assert lib.tg_gemm_fp8(*args(sa=float("inf"))) == tg.TG_ERR_INVALID_VALUE
+    assert lib.tg_gemm_fp8(*args(lay=0)) == tg.TG_ERR_NOT_SUPPORTED
+    assert lib.tg_gemm_fp8(*args(M=0)) == tg.TG_OK
+    # fp8 rows of 8 elements are only 8 bytes: misaligned leading dimension
+    assert lib.tg_gemm_fp8(8, 8, 8, A16, 8, A16, 16, 1, 1.0, 1.0, A16, 8, 0, None) == tg.TG_ERR_MISALIGNED
+
+
+def test_w4a16_validation(tg):
+    lib = tg.lib
+
+    def call(M=4, N=8, K=128, A=A16, lda=128, q=A16, ldq=16, s=A16, lds=1, g=128, zp=8, C=A16, ldc=8):
+        return lib.tg_gemm_w4a16(M, N, K, A, lda, q, ldq, s, lds, g, zp, C, ldc, None)
+
+    assert call(M=-1) == tg.TG_ERR_INVALID_VALUE
+    assert call(g=64) == tg.TG_ERR_NOT_SUPPORTED
+    assert call(K=200) == tg.TG_ERR_NOT_SUPPORTED
+    assert call(zp=16) == tg.TG_ERR_NOT_SUPPORTED
+    assert call(q=None) == tg.TG_ERR_INVALID_VALUE
+    assert call(ldq=8) == tg.TG_ERR_INVALID_VALUE
+    assert call(lds=0) == tg.TG_ERR_INVALID_VALUE
+    assert call(ldq=17) == tg.TG_ERR_MISALIGNED
+    assert call(s=A16 + 1) == tg.TG_ERR_MISALIGNED
+    assert call(A=A16 + 2) == tg.TG_ERR_MISALIGNED
+    assert call(ldc=4) == tg.TG_ERR_INVALID_VALUE
+    assert call(M=0) == tg.TG_OK
+    assert lib.tg_dequant_w4(8, 128, A16, 16, A16, 1, 128, 8, None, 128, None) == tg.TG_ERR_INVALID_VALUE
+    assert lib.tg_dequant_w4(8, 128, A16, 16, A16, 1, 128, 8, A16 + 2, 128, None) == tg.TG_ERR_MISALIGNED
+    assert lib.tg_dequant_w4(8, 100, A16, 16, A16, 1, 128, 8, A16, 128, None) == tg.TG_ERR_NOT_SUPPORTED
+    assert lib.tg_dequant_w4(0, 128, None, 16, None, 1, 128, 8, None, 128, None) == tg.TG_OK
+
+
+def test_product_and_oracle_share_no_code():
+    """The oracle is independent of the HIP path: neither imports the other."""
+    pkg = os.path.join(ROOT, "tile_level_gemm_02_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "oracle.c" not in text and "liboracle" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(ROOT, "oracle", f), encoding="utf-8").read()
+            assert not re.search(r"^\s*(import|from)\s+tile_level_gemm_02_amd\b", text, re.M), f
+            assert not re.search(r"#\s*include\s*[<\"].*tg(_\w+)?\.h", text), f
+            assert "libtg" not in text, f

@@ -1,0 +1,179 @@
+"""tile_level_gemm_02_amd -- Python binding of libtg.so, the MI355X tile GEMM library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/tg.h.  torch supplies device
+memory and the current HIP stream.  There is no fallback: if libtg.so is
+missing or fails to load, importing this package raises.
+
+Entry points (same names as the C ABI):
+
+    tg_gemm_f16(A, B, C, b_layout="row"|"col", stream=None)
+    tg_gemm_bf16(A, B, C, b_layout="row"|"col", stream=None)
+    tg_gemm_fp8(A, B, C, scale_a, scale_b, b_layout="col", stream=None)
+    tg_gemm_w4a16(A, qweight, scales, C, group_size=128, zero_point=8, stream=None)
+    tg_dequant_w4(qweight, scales, W, K, group_size=128, zero_point=8, stream=None)
+    tg_status_string(code), tg_version()
+
+Tensor conventions: A is M x K; for b_layout "row" B is the K x N matrix, for
+"col" B is its N x K storage (the transpose_B / nn.Linear layout); C is M x N
+and its dtype (float32, float16, bfloat16) selects the output type.  Every
+matrix must have unit stride along its last dimension; the other stride is
+the leading dimension.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime that libtg.so then shares
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtg.so")
+
+TG_OK, TG_ERR_INVALID_VALUE, TG_ERR_NOT_SUPPORTED, TG_ERR_MISALIGNED, TG_ERR_LAUNCH = range(5)
+TG_F32, TG_F16, TG_BF16 = 0, 1, 2
+TG_ROW_MAJOR, TG_COL_MAJOR = 0, 1
+
+EXPORTS = ("tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16", "tg_dequant_w4",
+           "tg_status_string", "tg_version")
+
+
+class TGError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn}: {tg_status_string(code)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m tile_level_gemm_02_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, f32, ci = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    dense = [i64, i64, i64, vp, i64, vp, i64, ci, vp, i64, ci, vp]
+    lib.tg_gemm_f16.argtypes = dense
+    lib.tg_gemm_bf16.argtypes = dense
+    lib.tg_gemm_fp8.argtypes = [i64, i64, i64, vp, i64, vp, i64, ci, f32, f32, vp, i64, ci, vp]
+    lib.tg_gemm_w4a16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, i32, vp, i64, vp]
+    lib.tg_dequant_w4.argtypes = [i64, i64, vp, i64, vp, i64, i32, i32, vp, i64, vp]
+    for name in ("tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16", "tg_dequant_w4"):
+        getattr(lib, name).restype = ci
+    lib.tg_status_string.argtypes = [ci]
+    lib.tg_status_string.restype = ctypes.c_char_p
+    lib.tg_version.argtypes = []
+    lib.tg_version.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def tg_status_string(code: int) -> str:
+    return lib.tg_status_string(int(code)).decode()
+
+
+def tg_version() -> int:
+    return int(lib.tg_version())
+
+
+# ------------------------------------------------------------- marshalling
+
+_CDTYPE = {torch.float32: TG_F32, torch.float16: TG_F16, torch.bfloat16: TG_BF16}
+
+
+def _mat(t: torch.Tensor, name: str):
+    """(rows, cols, leading dimension, device pointer) of a 2-D matrix view."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last dimension")
+    ld = t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+    return t.shape[0], t.shape[1], ld, t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ok(fn: str, code: int) -> None:
+    if code != TG_OK:
+        raise TGError(fn, code)
+
+
+def _dense(fn_name: str, A, B, C, b_layout: str, stream):
+    M, K, lda, pa = _mat(A, "A")
+    if b_layout == "row":
+        Kb, N, ldb, pb = _mat(B, "B")
+        lay = TG_ROW_MAJOR
+    elif b_layout == "col":
+        N, Kb, ldb, pb = _mat(B, "B")
+        lay = TG_COL_MAJOR
+    else:
+        raise ValueError("b_layout must be 'row' or 'col'")
+    if Kb != K:
+        raise ValueError(f"inner sizes differ: A has K={K}, B has K={Kb}")
+    Mc, Nc, ldc, pc = _mat(C, "C")
+    if (Mc, Nc) != (M, N):
+        raise ValueError(f"C must be {M}x{N}, got {Mc}x{Nc}")
+    if C.dtype not in _CDTYPE:
+        raise ValueError(f"unsupported C dtype {C.dtype}")
+    return M, N, K, pa, lda, pb, ldb, lay, pc, ldc, _CDTYPE[C.dtype], _stream(stream)
+
+
+def tg_gemm_f16(A, B, C, b_layout: str = "row", stream=None) -> None:
+    """C = A.B with fp16 A, B (fp32 accumulate); see include/tg.h."""
+    if A.dtype != torch.float16 or B.dtype != torch.float16:
+        raise ValueError("tg_gemm_f16 takes float16 A and B")
+    _ok("tg_gemm_f16", lib.tg_gemm_f16(*_dense("tg_gemm_f16", A, B, C, b_layout, stream)))
+
+
+def tg_gemm_bf16(A, B, C, b_layout: str = "row", stream=None) -> None:
+    """C = A.B with bf16 A, B (fp32 accumulate); see include/tg.h."""
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise ValueError("tg_gemm_bf16 takes bfloat16 A and B")
+    _ok("tg_gemm_bf16", lib.tg_gemm_bf16(*_dense("tg_gemm_bf16", A, B, C, b_layout, stream)))
+
+
+def tg_gemm_fp8(A, B, C, scale_a: float, scale_b: float, b_layout: str = "col", stream=None) -> None:
+    """C = scale_a*scale_b * A.B with e4m3 A, B (fp32 accumulate); see include/tg.h."""
+    if A.dtype != torch.float8_e4m3fn or B.dtype != torch.float8_e4m3fn:
+        raise ValueError("tg_gemm_fp8 takes float8_e4m3fn A and B")
+    M, N, K, pa, lda, pb, ldb, lay, pc, ldc, cd, st = _dense("tg_gemm_fp8", A, B, C, b_layout, stream)
+    _ok("tg_gemm_fp8", lib.tg_gemm_fp8(M, N, K, pa, lda, pb, ldb, lay, float(scale_a), float(scale_b),
+                                       pc, ldc, cd, st))
+
+
+def tg_gemm_w4a16(A, qweight, scales, C, group_size: int = 128, zero_point: int = 8, stream=None) -> None:
+    """C (fp16) = A . dequant(qweight, scales); qweight int32 [N][K/8], scales fp16 [N][K/g]."""
+    if A.dtype != torch.float16 or C.dtype != torch.float16:
+        raise ValueError("tg_gemm_w4a16 takes float16 A and C")
+    if qweight.dtype != torch.int32 or scales.dtype != torch.float16:
+        raise ValueError("qweight must be int32 and scales float16")
+    M, K, lda, pa = _mat(A, "A")
+    N, _, ldq, pq = _mat(qweight, "qweight")
+    Ns, _, lds, ps = _mat(scales, "scales")
+    Mc, Nc, ldc, pc = _mat(C, "C")
+    if Ns != N or (Mc, Nc) != (M, N):
+        raise ValueError("inconsistent w4a16 shapes")
+    _ok("tg_gemm_w4a16", lib.tg_gemm_w4a16(M, N, K, pa, lda, pq, ldq, ps, lds, int(group_size),
+                                           int(zero_point), pc, ldc, _stream(stream)))
+
+
+def tg_dequant_w4(qweight, scales, W, K: int | None = None, group_size: int = 128, zero_point: int = 8,
+                  stream=None) -> None:
+    """W (fp16 [N][K]) = dequant(qweight, scales), bit-identical to the GEMM's weights."""
+    if qweight.dtype != torch.int32 or scales.dtype != torch.float16 or W.dtype != torch.float16:
+        raise ValueError("qweight int32, scales float16, W float16 expected")
+    N, _, ldq, pq = _mat(qweight, "qweight")
+    Ns, _, lds, ps = _mat(scales, "scales")
+    Nw, Kw, ldw, pw = _mat(W, "W")
+    K = Kw if K is None else K
+    if Ns != N or Nw != N or Kw != K:
+        raise ValueError("inconsistent dequant shapes")
+    _ok("tg_dequant_w4", lib.tg_dequant_w4(N, K, pq, ldq, ps, lds, int(group_size), int(zero_point),
+                                           pw, ldw, _stream(stream)))

@@ -1,0 +1,204 @@
+// Device-side building blocks shared by the tile GEMM kernels (gfx950 only).
+//
+// The kernels follow the dataflow of the single-GPU GEMM skeleton in
+// "TileScale 与 TileLang比较" (section 核心抽象与编程模型对比): one workgroup per
+// output tile, A and B K-slices staged in on-chip shared memory (LDS here), a
+// register accumulator cleared before the K loop, one tile product per K step,
+// one store of the accumulator at the end.  The compiler passes listed in the
+// section 编译与优化流水线 (shared-memory swizzle, vectorised copies,
+// software pipelining, tensorisation, tail splitting) are written out by hand
+// in these files for CDNA4: XOR-swizzled LDS rows, 128-bit global loads,
+// double-buffered LDS, MFMA instructions, and masked tails.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// element type of A and B
+enum Elem : int { E_F16 = 0, E_BF16 = 1, E_FP8 = 2 };
+// output type of C
+enum Out : int { O_F32 = 0, O_F16 = 1, O_BF16 = 2 };
+
+template <int E> struct ElemInfo;
+template <> struct ElemInfo<E_F16> { static constexpr int bytes = 2; };
+template <> struct ElemInfo<E_BF16> { static constexpr int bytes = 2; };
+template <> struct ElemInfo<E_FP8> { static constexpr int bytes = 1; };
+
+template <typename T, typename F> __device__ __forceinline__ T bit_cast(F f)
+{
+    static_assert(sizeof(T) == sizeof(F), "size");
+    return __builtin_bit_cast(T, f);
+}
+
+// ------------------------------------------------------------------ MFMA
+// One 32x32 output block += (32 x kstep) . (kstep x 32).  Lane l holds row
+// (l % 32) of A and column (l % 32) of B; both operands carry the same k
+// values per lane and register, so the k order inside a step is irrelevant
+// to the sum.  16-bit types: kstep 16, 8 elements per lane.  fp8: kstep 64,
+// 32 elements per lane.
+template <int E> struct Mfma32;
+template <> struct Mfma32<E_F16> {
+    typedef u32x4 frag;
+    __device__ __forceinline__ static f32x16 run(frag a, frag b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(bit_cast<f16x8>(a), bit_cast<f16x8>(b), c, 0, 0, 0);
+    }
+};
+template <> struct Mfma32<E_BF16> {
+    typedef u32x4 frag;
+    __device__ __forceinline__ static f32x16 run(frag a, frag b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bit_cast<bf16x8>(a), bit_cast<bf16x8>(b), c, 0, 0, 0);
+    }
+};
+template <> struct Mfma32<E_FP8> {
+    typedef i32x8 frag;
+    __device__ __forceinline__ static f32x16 run(frag a, frag b, f32x16 c)
+    {
+        // format codes 0/0: both operands OCP e4m3; scale arguments unused (0)
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    }
+};
+
+// Wait states between the last MFMA of a kernel and the first instruction that
+// reads its accumulators.  A 16-pass MFMA (the fp8 32x32x64 form) needs 18
+// before a VALU, VMEM or LDS instruction may read its result; 24 are spent
+// here unconditionally, once per kernel, instead of relying on the count the
+// compiler derives (a short count was observed for the fp8 form).
+__device__ __forceinline__ void mfma_drain()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// ------------------------------------------------------- output conversion
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x)
+{
+    uint32_t u = bit_cast<uint32_t>(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return 0x7FC0;  // NaN
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float x)
+{
+    return bit_cast<uint16_t>((_Float16)x);
+}
+
+template <int O> struct OutInfo;
+template <> struct OutInfo<O_F32> { typedef float T; };
+template <> struct OutInfo<O_F16> { typedef uint16_t T; };
+template <> struct OutInfo<O_BF16> { typedef uint16_t T; };
+
+template <int O> __device__ __forceinline__ typename OutInfo<O>::T convert_out(float x);
+template <> __device__ __forceinline__ float convert_out<O_F32>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t convert_out<O_F16>(float x) { return f32_to_f16_rne(x); }
+template <> __device__ __forceinline__ uint16_t convert_out<O_BF16>(float x) { return f32_to_bf16_rne(x); }
+
+// ------------------------------------------------------------ LDS swizzle
+// A staged tile row holds 128 bytes of K (8 chunks of 16 bytes).  Chunk c of
+// row r lives at chunk position c ^ (r & 7), so the 8 lanes that read one
+// chunk column from 8 consecutive rows hit 8 different 16-byte bank groups.
+__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk)
+{
+    return row * 128u + ((chunk ^ (row & 7u)) << 4);
+}
+
+// -------------------------------------------------------- masked loading
+// Load the 16-byte chunk of a K-contiguous row that starts at element k0,
+// keeping only elements with index < kmax (bytes beyond are zero).  Used
+// only on tails, where the full 16 bytes may run past the buffer.
+template <int EB>
+__device__ __forceinline__ u32x4 load_chunk_partial(const uint8_t* p, int64_t avail)
+{
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16 / EB; ++e) {
+        if (e < avail) {
+            uint32_t v = (EB == 2) ? (uint32_t)((const uint16_t*)p)[e] : (uint32_t)p[e];
+            w[(e * EB) >> 2] |= v << (((e * EB) & 3) * 8);
+        }
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ u32x4 ldg128(const void* p)
+{
+    return *(const u32x4*)p;
+}
+
+__device__ __forceinline__ void sts128(uint8_t* lds, uint32_t off, u32x4 v)
+{
+    *(u32x4*)(lds + off) = v;
+}
+
+__device__ __forceinline__ u32x4 lds128(const uint8_t* lds, uint32_t off)
+{
+    return *(const u32x4*)(lds + off);
+}
+
+// ------------------------------------------------------------ int4 dequant
+// Eight int4 weights of one 32-bit word -> eight fp16 values, in k order
+// (nibble j, bits 4j..4j+3, is k offset j).  Each nibble q is placed in the
+// fraction of the fp16 number 1024 + q (bits 0x6400 | q), the exact integer
+// (1024 + zero_point) is subtracted (exact: |q - zp| <= 15), and the result
+// is multiplied by the fp16 scale with one round-to-nearest-even step, which
+// is fp16_RNE((q - zp) * s).  Packed-half arithmetic, two weights per op.
+__device__ __forceinline__ u32x4 dequant_w4_word(uint32_t w, f16x2 zp_bias, f16x2 s2)
+{
+    uint32_t out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t lo = (w >> (8 * j)) & 0xFu;
+        uint32_t hi = (w >> (8 * j + 4)) & 0xFu;
+        uint32_t x = lo | (hi << 16) | 0x64006400u;
+        f16x2 h = bit_cast<f16x2>(x);
+        h = h - zp_bias;
+        h = h * s2;
+        out[j] = bit_cast<uint32_t>(h);
+    }
+    return u32x4{out[0], out[1], out[2], out[3]};
+}
+
+__device__ __forceinline__ f16x2 w4_zero_bias(int zero_point)
+{
+    _Float16 b = (_Float16)(1024 + zero_point);  // exact
+    return f16x2{b, b};
+}
+
+// ------------------------------------------------------- tile scheduling
+// Map the linear workgroup id to an output tile.  Workgroups are dealt to the
+// 8 XCDs of the chip round-robin (id % 8); consecutive ids are first regrouped
+// so that each XCD receives a contiguous range of tiles, and that range is
+// walked GROUP_M tile rows at a time so the tiles resident on one XCD share
+// rows of A and columns of B in that XCD's L2.
+__device__ __forceinline__ void tile_coords(uint32_t bid, uint32_t nblocks, uint32_t tiles_m,
+                                            uint32_t tiles_n, uint32_t group_m, uint32_t& tm,
+                                            uint32_t& tn)
+{
+    uint32_t idx = bid;
+    if ((nblocks & 7u) == 0u)
+        idx = (bid & 7u) * (nblocks >> 3) + (bid >> 3);
+    uint32_t per_group = group_m * tiles_n;
+    uint32_t g = idx / per_group;
+    uint32_t first_m = g * group_m;
+    uint32_t gsize = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+    uint32_t r = idx - g * per_group;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+}
+
+}  // namespace tg

@@ -1,0 +1,153 @@
+// Host-side helpers of the C ABI: argument validation and kernel launch.
+// Validation runs before any HIP call, so a rejected call launches nothing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tg.h"
+#include "tg_kernels.hpp"
+
+namespace tg {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0u; }
+
+inline int out_bytes(tg_dtype d) { return d == TG_F32 ? 4 : 2; }
+
+// Validate a dense GEMM call (A: M x K, B: K x N in `b_layout`, C: M x N).
+// Returns TG_OK and sets *empty when nothing is to be computed.
+inline tg_status check_dense(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                             const void* B, int64_t ldb, int b_layout, void* C, int64_t ldc,
+                             int c_dtype, int elem_bytes, bool* empty)
+{
+    *empty = false;
+    if (M < 0 || N < 0 || K < 0)
+        return TG_ERR_INVALID_VALUE;
+    if (b_layout != TG_ROW_MAJOR && b_layout != TG_COL_MAJOR)
+        return TG_ERR_INVALID_VALUE;
+    if (c_dtype != TG_F32 && c_dtype != TG_F16 && c_dtype != TG_BF16)
+        return TG_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) {
+        *empty = true;
+        return TG_OK;
+    }
+    if (C == nullptr || ldc < N)
+        return TG_ERR_INVALID_VALUE;
+    if (K > 0) {
+        if (A == nullptr || B == nullptr)
+            return TG_ERR_INVALID_VALUE;
+        if (lda < K)
+            return TG_ERR_INVALID_VALUE;
+        if (ldb < (b_layout == TG_ROW_MAJOR ? N : K))
+            return TG_ERR_INVALID_VALUE;
+        if (!aligned16(A) || !aligned16(B) || ((lda * elem_bytes) & 15) || ((ldb * elem_bytes) & 15))
+            return TG_ERR_MISALIGNED;
+    }
+    if (!aligned16(C) || ((ldc * out_bytes((tg_dtype)c_dtype)) & 15))
+        return TG_ERR_MISALIGNED;
+    return TG_OK;
+}
+
+inline tg_status launched()
+{
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+template <int BM, int BN>
+inline int64_t n_tiles(int64_t M, int64_t N)
+{
+    return ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+}
+
+template <int E, int BL, int O, int BM, int BN, bool W4>
+tg_status launch_tile(const TileArgs& a, hipStream_t s)
+{
+    const int64_t tiles = n_tiles<BM, BN>(a.M, a.N);
+    if (tiles > 0x7FFFFFFF)
+        return TG_ERR_NOT_SUPPORTED;
+    hipLaunchKernelGGL((tile_gemm<E, BL, O, BM, BN, W4>), dim3((uint32_t)tiles), dim3(kThreads), 0, s, a);
+    return launched();
+}
+
+// Tile edge for a dense problem: the largest tile that still gives enough
+// workgroups to spread over the chip's 256 compute units.
+inline int pick_tile(int64_t M, int64_t N, bool allow256)
+{
+    if (allow256 && n_tiles<256, 256>(M, N) >= 192)
+        return 256;
+    if (n_tiles<128, 128>(M, N) >= 96)
+        return 128;
+    return 64;
+}
+
+template <int E, int BL, int O>
+tg_status launch_tile_sized(TileArgs& a, hipStream_t s)
+{
+    const int t = pick_tile(a.M, a.N, BL == B_KCONTIG);
+    a.group_m = 4;
+    if constexpr (BL == B_KCONTIG) {
+        if (t == 256)
+            return launch_tile<E, BL, O, 256, 256, false>(a, s);
+    }
+    if (t >= 128)
+        return launch_tile<E, BL, O, 128, 128, false>(a, s);
+    return launch_tile<E, BL, O, 64, 64, false>(a, s);
+}
+
+template <int E, int BL>
+tg_status launch_dense(TileArgs& a, int c_dtype, hipStream_t s)
+{
+    switch (c_dtype) {
+    case TG_F32: return launch_tile_sized<E, BL, O_F32>(a, s);
+    case TG_F16: return launch_tile_sized<E, BL, O_F16>(a, s);
+    default: return launch_tile_sized<E, BL, O_BF16>(a, s);
+    }
+}
+
+// fp16 / bf16 GEMM.  M <= 16 against a K-contiguous B takes the skinny
+// kernel; everything else the tile kernel (K == 0 runs it with no K steps,
+// which stores zeros: the empty sum).
+template <int E>
+tg_status gemm_16bit(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, int b_layout, void* C, int64_t ldc, int c_dtype, void* stream)
+{
+    bool empty;
+    tg_status st = check_dense(M, N, K, A, lda, B, ldb, b_layout, C, ldc, c_dtype, 2, &empty);
+    if (st != TG_OK || empty)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (M <= 16 && b_layout == TG_COL_MAJOR && K > 0) {
+        SkinnyArgs sa{M, N, K, (const uint8_t*)A, lda, (const uint8_t*)B, ldb, C, ldc};
+        const int64_t blocks = (N + 15) / 16;
+        if (blocks > 0x7FFFFFFF)
+            return TG_ERR_NOT_SUPPORTED;
+        switch (c_dtype) {
+        case TG_F32:
+            hipLaunchKernelGGL((skinny_gemm<E, O_F32, 8, 8>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
+            break;
+        case TG_F16:
+            hipLaunchKernelGGL((skinny_gemm<E, O_F16, 8, 8>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
+            break;
+        default:
+            hipLaunchKernelGGL((skinny_gemm<E, O_BF16, 8, 8>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
+            break;
+        }
+        return launched();
+    }
+    TileArgs a{};
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.A = (const uint8_t*)A;
+    a.lda = lda;
+    a.B = (const uint8_t*)B;
+    a.ldb = ldb;
+    a.C = C;
+    a.ldc = ldc;
+    a.alpha = 1.0f;
+    if (b_layout == TG_COL_MAJOR)
+        return launch_dense<E, B_KCONTIG>(a, c_dtype, s);
+    return launch_dense<E, B_NCONTIG>(a, c_dtype, s);
+}
+
+}  // namespace tg

@@ -1,0 +1,110 @@
+// tg_gemm_w4a16 and tg_dequant_w4 (contract in include/tg.h).  Both run the
+// same device routine, tg::dequant_w4_word, so the GEMM's weights are
+// bit-identical to what tg_dequant_w4 writes.
+#include "tg_host.hpp"
+
+namespace tg {
+
+__global__ __launch_bounds__(256) void dequant_w4_kernel(DequantArgs p)
+{
+    const int64_t words = p.K / 8;
+    const int64_t total = p.N * words;
+    const f16x2 bias = w4_zero_bias(p.zero_point);
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256) {
+        const int64_t n = t / words, w = t - n * words;
+        const uint32_t q = p.qw[n * p.ldq + w];
+        const _Float16 s = bit_cast<_Float16>(p.scales[n * p.lds + (w * 8) / p.group_size]);
+        *(u32x4*)(p.W + n * p.ldw + w * 8) = dequant_w4_word(q, bias, f16x2{s, s});
+    }
+}
+
+}  // namespace tg
+
+namespace {
+
+tg_status check_w4(int64_t N, int64_t K, const int32_t* qweight, int64_t ldq, const void* scales,
+                   int64_t lds, int32_t group_size, int32_t zero_point)
+{
+    if (N < 0 || K < 0)
+        return TG_ERR_INVALID_VALUE;
+    if (group_size != 128 || (K % 128) != 0 || zero_point < 0 || zero_point > 15)
+        return TG_ERR_NOT_SUPPORTED;
+    if (N > 0 && K > 0) {
+        if (qweight == nullptr || scales == nullptr)
+            return TG_ERR_INVALID_VALUE;
+        if (ldq < K / 8 || lds < K / group_size)
+            return TG_ERR_INVALID_VALUE;
+        if (!tg::aligned16(qweight) || ((ldq * 4) & 15) || ((uintptr_t)scales & 1u))
+            return TG_ERR_MISALIGNED;
+    }
+    return TG_OK;
+}
+
+}  // namespace
+
+extern "C" tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                   const int32_t* qweight, int64_t ldq, const void* scales,
+                                   int64_t lds, int32_t group_size, int32_t zero_point, void* C,
+                                   int64_t ldc, void* stream)
+{
+    if (M < 0)
+        return TG_ERR_INVALID_VALUE;
+    tg_status st = check_w4(N, K, qweight, ldq, scales, lds, group_size, zero_point);
+    if (st != TG_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    if (C == nullptr || ldc < N)
+        return TG_ERR_INVALID_VALUE;
+    if (K > 0) {
+        if (A == nullptr || lda < K)
+            return TG_ERR_INVALID_VALUE;
+        if (!tg::aligned16(A) || ((lda * 2) & 15))
+            return TG_ERR_MISALIGNED;
+    }
+    if (!tg::aligned16(C) || ((ldc * 2) & 15))
+        return TG_ERR_MISALIGNED;
+    tg::TileArgs a{};
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.A = (const uint8_t*)A;
+    a.lda = lda;
+    a.C = C;
+    a.ldc = ldc;
+    a.alpha = 1.0f;
+    a.group_m = 4;
+    a.qw = (const uint32_t*)qweight;
+    a.ldq = ldq;
+    a.scales = (const uint16_t*)scales;
+    a.lds = lds;
+    a.zero_point = zero_point;
+    hipStream_t s = (hipStream_t)stream;
+    if (tg::n_tiles<128, 128>(M, N) >= 96)
+        return tg::launch_tile<tg::E_F16, tg::B_KCONTIG, tg::O_F16, 128, 128, true>(a, s);
+    return tg::launch_tile<tg::E_F16, tg::B_KCONTIG, tg::O_F16, 64, 64, true>(a, s);
+}
+
+extern "C" tg_status tg_dequant_w4(int64_t N, int64_t K, const int32_t* qweight, int64_t ldq,
+                                   const void* scales, int64_t lds, int32_t group_size,
+                                   int32_t zero_point, void* W, int64_t ldw, void* stream)
+{
+    tg_status st = check_w4(N, K, qweight, ldq, scales, lds, group_size, zero_point);
+    if (st != TG_OK)
+        return st;
+    if (N == 0 || K == 0)
+        return TG_OK;
+    if (W == nullptr || ldw < K)
+        return TG_ERR_INVALID_VALUE;
+    if (!tg::aligned16(W) || ((ldw * 2) & 15))
+        return TG_ERR_MISALIGNED;
+    tg::DequantArgs d{N, K, (const uint32_t*)qweight, ldq, (const uint16_t*)scales, lds,
+                      group_size, zero_point, (uint16_t*)W, ldw};
+    const int64_t words = N * (K / 8);
+    int64_t blocks = (words + 255) / 256;
+    if (blocks > 65536)
+        blocks = 65536;  // grid-stride loop covers the rest
+    hipLaunchKernelGGL(tg::dequant_w4_kernel, dim3((uint32_t)blocks), dim3(256), 0,
+                       (hipStream_t)stream, d);
+    return tg::launched();
+}
