@@ -186,6 +186,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
+                    help="only run plain device-to-device copies of MIB MiB (to scale HBM byte counters)")
+    ap.add_argument("--only", choices=["bf16_4096", "bf16_skinny", "fp8_8192", "w4a16"], default=None,
+                    help="only run this workload's launches (for counter collection), no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -199,7 +203,28 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_calibrate:
+        n = args.copy_calibrate << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch_read": n, "copy_bytes_per_launch_written": n,
+                          "launches": args.steps}), flush=True)
+        return
     flush = make_flush()
+    if args.only:
+        setup = {"bf16_4096": setup_bf16_4096, "bf16_skinny": setup_skinny, "fp8_8192": setup_fp8,
+                 "w4a16": setup_w4a16}[args.only]
+        _, fn, _, _ = setup()
+        for _ in range(args.warmup):
+            fn()
+        for _ in range(args.steps):
+            flush()
+            fn()
+        torch.cuda.synchronize()
+        return
 
     # ---- headline: bf16 4096^3
     w, fn, flops, nbytes = setup_bf16_4096()

@@ -1,5 +1,5 @@
 // Library-wide entry points that launch nothing (contract in include/tg.h).
-#include "../../include/tg.h"
+#include "tg.h"
 
 extern "C" const char* tg_status_string(tg_status status)
 {

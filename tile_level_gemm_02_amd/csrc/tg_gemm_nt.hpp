@@ -1,0 +1,358 @@
+// The main tile GEMM for K-contiguous operands ("NT": A row-major M x K, B
+// stored N x K -- the transpose_B form of the local GEMMs in the
+// "project_analysis.md" note on TileScale, SUMMA and Cannon examples), the
+// layout of the bf16 and fp8 workloads.
+//
+// Dataflow of the single-GPU GEMM skeleton in "TileScale 与 TileLang比较"
+// (section 核心抽象与编程模型对比), mapped onto CDNA4:
+//
+//  * grid of output tiles: one 256-thread workgroup (4 waves, 2 x 2) per
+//    BM x BN tile, ordered XCD-aware (tile_coords);
+//  * global -> shared copy: buffer loads that write LDS directly (no
+//    registers, no ds_write), 16 bytes per lane, 8 rows of 128 bytes per wave
+//    instruction, into XOR-swizzled rows; tails need no branches: rows past
+//    M or N are clamped to the last valid row (they only feed outputs that are
+//    never stored), 16-byte chunks past K read through an out-of-range offset,
+//    which the buffer unit returns as zeros;
+//  * pipelined K loop: two LDS stages; the loads of step k+2 are issued right
+//    after the barrier that retires step k, so each step's copy overlaps a
+//    full step of MFMAs;
+//  * tile GEMM into register fragments: LDS -> VGPR fragments double-buffered
+//    across the K sub-steps (the reads of sub-step s+1 are in flight while
+//    the MFMAs of sub-step s run), 32x32 MFMAs accumulating in fp32 AGPRs;
+//    the one barrier per K step sits before the last sub-step's MFMAs, which
+//    hide its skew and the first reads of the next step;
+//  * epilogue: scale (fp8), round to the output type, masked stores.
+#pragma once
+
+#include <type_traits>
+
+#include "tg_kernels.hpp"
+
+namespace tg {
+
+// offset beyond any valid byte of a buffer resource whose num_records is kNumRecords
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int32_t kNumRecords = 0x7FFFFFF0;
+constexpr int32_t kBufferFlags = 0x00020000;  // gfx9 raw buffer, 32-bit data format
+
+typedef __attribute__((address_space(3))) uint8_t* lds_u8_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (wave-uniform): base, stride 0, num_records, flags.
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base)
+{
+    const uint64_t a = (uint64_t)base;
+    return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                   __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF), kNumRecords, kBufferFlags};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(uint8_t* p)
+{
+    return (uint32_t)(uintptr_t)(lds_u8_t)p;
+}
+
+// One wave instruction: 64 lanes x 16 bytes from global memory straight into
+// the 1 KiB of LDS at `dst` (lane i lands at dst + 16*i).  Issued from inline
+// assembly so that the compiler does not track it: it would otherwise wait
+// for every outstanding copy before each LDS read, and it does not order the
+// copies of other waves anyway.  The kernel waits for its copies explicitly
+// (wait_copies) before the barrier that publishes them.
+__device__ __forceinline__ void load_lds_1k(i32x4_t r, uint8_t* dst, uint32_t voff, uint32_t soff)
+{
+    // M0 carries the LDS destination; one wait state between writing M0 and the copy
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                   "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(dst)))
+                 : "memory");
+}
+
+__device__ __forceinline__ void wait_copies()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int E, int O, int BM, int BN>
+__global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
+{
+    constexpr int EB = ElemInfo<E>::bytes;
+    constexpr int CE = 16 / EB;   // elements per 16-byte chunk
+    constexpr int KE = 128 / EB;  // K elements per step (128 bytes of a row)
+    constexpr int TM = BM / 64, TN = BN / 64;
+    constexpr int AI = BM / 32, BI = BN / 32;  // LDS-DMA instructions per wave per step
+    constexpr int STAGE = (BM + BN) * 128;
+    constexpr int KSTEPS = (E == E_FP8) ? 2 : 4;
+    typedef typename Mfma32<E>::frag Frag;
+    typedef typename OutInfo<O>::T OutT;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
+
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases scalar
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
+    const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
+    uint32_t tmi, tni;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, p.group_m, tmi, tni);
+    const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
+    const uint32_t ldab = (uint32_t)(p.lda * EB), ldbb = (uint32_t)(p.ldb * EB);
+    const int32_t rows_a = (int32_t)(M - m0 < BM ? M - m0 : BM);
+    const int32_t rows_b = (int32_t)(N - n0 < BN ? N - n0 : BN);
+    const i32x4_t ra = make_rsrc(p.A + m0 * (int64_t)ldab);
+    const i32x4_t rb = make_rsrc(p.B + n0 * (int64_t)ldbb);
+    const int64_t KT = (K + KE - 1) / KE;  // K is a multiple of CE on this path
+
+    // ---- source offsets of the LDS-DMA instructions
+    // Wave w fills rows [w*BM/4, (w+1)*BM/4) of the A stage (and likewise of
+    // B), 8 rows per instruction.  Lane i lands at physical chunk i%8 of row
+    // i/8 of the instruction's 8 rows.  Rows are swizzled with row_swz(): a
+    // row's logical chunk c sits at physical chunk c ^ ((row/2) % 8), so the
+    // swizzle is applied on the source side: lane i loads logical chunk
+    // (i%8) ^ ((row/2) % 8), which for the rows of instruction j is
+    // (i%8) ^ ((4j + (i/8)/2) % 8) -- one value for even j, one for odd j.
+    // The per-lane part of the offset is fixed; the step's K offset and the
+    // instruction's 8-row block go into the scalar offset.  Rows past M or N:
+    // on edge tiles their lanes read through an out-of-range offset (zeros);
+    // they only feed outputs that are never stored.
+    const uint32_t lrow8 = lane >> 3;
+    const uint32_t lchunk0 = (lane & 7u) ^ (lrow8 >> 1);
+    const uint32_t lchunk1 = (lane & 7u) ^ (4u + (lrow8 >> 1));
+    const uint32_t va0 = (wave * (BM / 4) + lrow8) * ldab + lchunk0 * 16u;
+    const uint32_t va1 = (wave * (BM / 4) + lrow8) * ldab + lchunk1 * 16u;
+    const uint32_t vb0 = (wave * (BN / 4) + lrow8) * ldbb + lchunk0 * 16u;
+    const uint32_t vb1 = (wave * (BN / 4) + lrow8) * ldbb + lchunk1 * 16u;
+
+    // copy instruction j (of AI) of operand A, or of BI of operand B, for K step kt into stage `st`
+    auto chunk_oob = [&](int64_t kt, uint32_t lchunk) __attribute__((always_inline)) -> uint32_t {
+        // a chunk at or past K (only in the last step) reads through an
+        // out-of-range offset (bit 31 set): zeros.  Valid offsets stay below 2^31.
+        const int64_t kleft = K - kt * KE;
+        const uint32_t kmax = kleft >= KE ? (uint32_t)KE : (uint32_t)kleft;
+        return (lchunk * CE < kmax) ? 0u : kOutOfRange;
+    };
+    // a copy for a step past the last one reads through the out-of-range offset:
+    // it only writes zeros into a buffer that is not read again
+    auto copy_a = [&](auto edge, int64_t kt, uint8_t* st, int j) __attribute__((always_inline)) {
+        uint32_t v = (j & 1) ? (va1 | chunk_oob(kt, lchunk1)) : (va0 | chunk_oob(kt, lchunk0));
+        v |= kt < KT ? 0u : kOutOfRange;
+        if constexpr (decltype(edge)::value)
+            v |= (int32_t)(wave * (BM / 4) + 8 * j + lrow8) < rows_a ? 0u : kOutOfRange;
+        load_lds_1k(ra, st + wave * (BM / 4) * 128 + j * 1024, v, (uint32_t)kt * 128u + (uint32_t)(8 * j) * ldab);
+    };
+    auto copy_b = [&](auto edge, int64_t kt, uint8_t* st, int j) __attribute__((always_inline)) {
+        uint32_t v = (j & 1) ? (vb1 | chunk_oob(kt, lchunk1)) : (vb0 | chunk_oob(kt, lchunk0));
+        v |= kt < KT ? 0u : kOutOfRange;
+        if constexpr (decltype(edge)::value)
+            v |= (int32_t)(wave * (BN / 4) + 8 * j + lrow8) < rows_b ? 0u : kOutOfRange;
+        load_lds_1k(rb, st + BM * 128 + wave * (BN / 4) * 128 + j * 1024, v,
+                    (uint32_t)kt * 128u + (uint32_t)(8 * j) * ldbb);
+    };
+
+    // ---- fragment reads: every fragment row of this lane has the same (row/2)%8
+    const uint32_t wm = wave >> 1, wn = wave & 1u;
+    const uint32_t lrow = lane & 31u, lgrp = lane >> 5;
+    const uint32_t sw = (lrow >> 1) & 7u;
+    const uint32_t a_row0 = (wm * (BM / 2) + lrow) * 128u;
+    const uint32_t b_row0 = BM * 128u + (wn * (BN / 2) + lrow) * 128u;
+
+    Frag fa[2][TM], fb[2][TN];
+    auto read_frags = [&](const uint8_t* st, int s, int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            if constexpr (E == E_FP8) {
+                const uint32_t c0 = (uint32_t)(4 * s) + 2u * lgrp;
+                const u32x4 lo = lds128(st, a_row0 + i * 32 * 128 + ((c0 ^ sw) << 4));
+                const u32x4 hi = lds128(st, a_row0 + i * 32 * 128 + (((c0 + 1u) ^ sw) << 4));
+                fa[slot][i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            } else {
+                fa[slot][i] = lds128(st, a_row0 + i * 32 * 128 + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (E == E_FP8) {
+                const uint32_t c0 = (uint32_t)(4 * s) + 2u * lgrp;
+                const u32x4 lo = lds128(st, b_row0 + j * 32 * 128 + ((c0 ^ sw) << 4));
+                const u32x4 hi = lds128(st, b_row0 + j * 32 * 128 + (((c0 + 1u) ^ sw) << 4));
+                fb[slot][j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            } else {
+                fb[slot][j] = lds128(st, b_row0 + j * 32 * 128 + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
+            }
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = f32x16{};
+
+    // acc[i][j] holds the transposed 32x32 block (B rows x A rows): value v of
+    // lane l is C[m = i*32 + l%32][n = j*32 + 8*(v/4) + 4*(l/32) + v%4], so every
+    // lane owns runs of 4 consecutive output columns.
+    // The TM*TN MFMAs of one sub-step; the calls `between(q)` (q = 0 .. NQ-1)
+    // are spread evenly over them and pinned in place, so copies interleave
+    // with the matrix instructions instead of stalling the wave's in-order
+    // issue in one burst.
+    auto mma = [&](int slot, auto between, auto nq) __attribute__((always_inline)) {
+        constexpr int NQ = decltype(nq)::value;
+#pragma unroll
+        for (int t = 0; t < TM * TN; ++t) {
+            const int i = t / TN, j = t % TN;
+            acc[i][j] = Mfma32<E>::run(fb[slot][j], fa[slot][i], acc[i][j]);
+            if constexpr (NQ > 0) {
+                const int q0 = t * NQ / (TM * TN), q1 = (t + 1) * NQ / (TM * TN);
+                if (q1 > q0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    for (int q = q0; q < q1; ++q)
+                        between(q);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    };
+    auto nothing = [](int) {};
+
+    // One K step out of `cur`.  Entering, the fragments of its sub-step 0 are
+    // in slot 0 and the A copies of step kt+1 (into `nxt`) are in flight; the
+    // B copies of step kt+1 are issued between the sub-step-0 MFMAs.  After the
+    // barrier, the A copies of step kt+2 (into `cur`, now free) go out between
+    // the last sub-step's MFMAs, and the first fragments of step kt+1 are read
+    // (harmlessly, from a stale buffer, after the last step).
+    auto step = [&](auto edge, int64_t kt, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < KSTEPS - 1; ++s) {
+            read_frags(cur, s + 1, (s + 1) & 1);
+            if (s == 0)
+                mma(s & 1, [&](int q) __attribute__((always_inline)) { copy_b(edge, kt + 1, nxt, q); },
+                    std::integral_constant<int, BI>{});
+            else
+                mma(s & 1, nothing, std::integral_constant<int, 0>{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_copies();    // own copies of step kt+1 landed ...
+        __syncthreads();  // ... and every wave's; every wave is done reading `cur`
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(nxt, 0, 0);
+        mma((KSTEPS - 1) & 1, [&](int q) __attribute__((always_inline)) { copy_a(edge, kt + 2, cur, q); },
+            std::integral_constant<int, AI>{});
+    };
+
+    auto run = [&](auto edge) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < AI; ++j)
+            copy_a(edge, 0, lds0, j);
+#pragma unroll
+        for (int j = 0; j < BI; ++j)
+            copy_b(edge, 0, lds0, j);
+#pragma unroll
+        for (int j = 0; j < AI; ++j)
+            copy_a(edge, 1, lds1, j);
+        wait_copies();
+        __syncthreads();
+        read_frags(lds0, 0, 0);
+        for (int64_t kt = 0; kt < KT; kt += 2) {
+            step(edge, kt, lds0, lds1);
+            if (kt + 1 < KT)
+                step(edge, kt + 1, lds1, lds0);
+        }
+        wait_copies();  // copies past the last step (zeros) must land before LDS is reused
+    };
+    if (KT > 0) {
+        if (rows_a == BM && rows_b == BN)
+            run(std::false_type{});
+        else
+            run(std::true_type{});
+    }
+    mfma_drain();
+
+    // ---- epilogue
+    constexpr int WR = BM / 2, WC = BN / 2;  // this wave's sub-tile
+    const int64_t wrow0 = m0 + wm * WR, wcol0 = n0 + wn * WC;
+    auto out_val = [&](int i, int j, int v) __attribute__((always_inline)) -> float {
+        float x = acc[i][j][v];
+        if constexpr (E == E_FP8)
+            x *= p.alpha;
+        return x;
+    };
+    if constexpr (O == O_F32) {
+        // 4 consecutive fp32 columns per lane: one 16-byte store each
+        float* C = (float*)p.C;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t row = wrow0 + i * 32 + lrow;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t col = wcol0 + j * 32 + 8 * g + 4 * lgrp;
+                    const f32x4 q = {out_val(i, j, 4 * g), out_val(i, j, 4 * g + 1), out_val(i, j, 4 * g + 2),
+                                     out_val(i, j, 4 * g + 3)};
+                    if (row < M) {
+                        if (col + 4 <= N) {
+                            *(f32x4*)(C + row * p.ldc + col) = q;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (col + e < N)
+                                    C[row * p.ldc + col + e] = q[e];
+                        }
+                    }
+                }
+            }
+        }
+    } else {
+        // 16-bit output: each wave stages its sub-tile in its own LDS region
+        // (row-major, 16-byte chunks XOR-swizzled by row), then writes whole
+        // rows with 16-byte stores.
+        constexpr int RB = WC * 2;       // bytes per staged row
+        constexpr int NCH = RB / 16;     // 16-byte chunks per row
+        constexpr int WBYTES = WR * RB;  // bytes per wave
+        constexpr int WPS = STAGE / WBYTES;  // waves per stage array
+        static_assert(2 * WPS >= 4, "epilogue staging must fit the two stage arrays");
+        __syncthreads();  // every wave is done reading the stage buffers
+        uint8_t* ep = (wave / WPS ? lds1 : lds0) + (wave % WPS) * WBYTES;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const uint32_t r = i * 32 + lrow;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t c = (uint32_t)(4 * j + g);  // 16-byte chunk of columns j*32 + 8g .. +7
+                    const uint32_t lo = (uint32_t)convert_out<O>(out_val(i, j, 4 * g)) |
+                                        ((uint32_t)convert_out<O>(out_val(i, j, 4 * g + 1)) << 16);
+                    const uint32_t hi = (uint32_t)convert_out<O>(out_val(i, j, 4 * g + 2)) |
+                                        ((uint32_t)convert_out<O>(out_val(i, j, 4 * g + 3)) << 16);
+                    *(u32x2*)(ep + r * RB + ((c ^ (r % NCH)) << 4) + lgrp * 8) = u32x2{lo, hi};
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes done
+        uint16_t* C = (uint16_t*)p.C;
+#pragma unroll
+        for (int t = 0; t < WR * NCH / 64; ++t) {
+            const uint32_t idx = t * 64 + lane;
+            const uint32_t r = idx / NCH, c = idx % NCH;
+            const u32x4 q = lds128(ep, r * RB + ((c ^ (r % NCH)) << 4));
+            const int64_t row = wrow0 + r, col = wcol0 + c * 8;
+            if (row < M) {
+                if (col + 8 <= N) {
+                    *(u32x4*)(C + row * p.ldc + col) = q;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (col + e < N)
+                            C[row * p.ldc + col + e] = (uint16_t)(q[e >> 1] >> ((e & 1) * 16));
+                }
+            }
+        }
+    }
+}
+
+}  // namespace tg

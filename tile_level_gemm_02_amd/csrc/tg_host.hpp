@@ -5,7 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/tg.h"
+#include "tg.h"
+#include "tg_gemm_nt.hpp"
 #include "tg_kernels.hpp"
 
 namespace tg {
@@ -94,9 +95,49 @@ tg_status launch_tile_sized(TileArgs& a, hipStream_t s)
     return launch_tile<E, BL, O, 64, 64, false>(a, s);
 }
 
+// The direct-to-LDS NT kernel needs whole 16-byte chunks along K and 32-bit
+// buffer offsets over one tile (BM rows of A / BN rows of B plus one K span).
+template <int E>
+inline bool nt_eligible(const TileArgs& a)
+{
+    constexpr int EB = ElemInfo<E>::bytes;
+    const int64_t lim = (int64_t)kNumRecords;
+    return (a.K % (16 / EB)) == 0 && 256 * a.lda * EB + a.K * EB < lim && 256 * a.ldb * EB + a.K * EB < lim;
+}
+
+template <int E, int O, int BM, int BN>
+tg_status launch_nt(const TileArgs& a, hipStream_t s)
+{
+    const int64_t tiles = n_tiles<BM, BN>(a.M, a.N);
+    if (tiles > 0x7FFFFFFF)
+        return TG_ERR_NOT_SUPPORTED;
+    hipLaunchKernelGGL((gemm_nt<E, O, BM, BN>), dim3((uint32_t)tiles), dim3(kThreads), 0, s, a);
+    return launched();
+}
+
+template <int E, int O>
+tg_status launch_nt_sized(TileArgs& a, hipStream_t s)
+{
+    a.group_m = 4;
+    switch (pick_tile(a.M, a.N, true)) {
+    case 256: return launch_nt<E, O, 256, 256>(a, s);
+    case 128: return launch_nt<E, O, 128, 128>(a, s);
+    default: return launch_nt<E, O, 64, 64>(a, s);
+    }
+}
+
 template <int E, int BL>
 tg_status launch_dense(TileArgs& a, int c_dtype, hipStream_t s)
 {
+    if constexpr (BL == B_KCONTIG) {
+        if (nt_eligible<E>(a)) {
+            switch (c_dtype) {
+            case TG_F32: return launch_nt_sized<E, O_F32>(a, s);
+            case TG_F16: return launch_nt_sized<E, O_F16>(a, s);
+            default: return launch_nt_sized<E, O_BF16>(a, s);
+            }
+        }
+    }
     switch (c_dtype) {
     case TG_F32: return launch_tile_sized<E, BL, O_F32>(a, s);
     case TG_F16: return launch_tile_sized<E, BL, O_F16>(a, s);
