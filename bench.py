@@ -264,7 +264,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": stored_traffic("bf16_4096"),
-                     "kernel": "tile_gemm<bf16, B col-major, bf16 out, 256x256>",
+                     "kernel": "gemm_nt<bf16, bf16 out, 256x256 tile, 2 LDS stages of 128 B rows>",
                      "flop_per_launch": flops, "avg_launch_us": round(avg_launch * 1e6, 3)},
     }
 

@@ -14,9 +14,10 @@
 //    M or N are clamped to the last valid row (they only feed outputs that are
 //    never stored), 16-byte chunks past K read through an out-of-range offset,
 //    which the buffer unit returns as zeros;
-//  * pipelined K loop: two LDS stages; the loads of step k+2 are issued right
-//    after the barrier that retires step k, so each step's copy overlaps a
-//    full step of MFMAs;
+//  * pipelined K loop: NST LDS stages of RB bytes of K per row; the copies of
+//    step k+NST-1 and k+NST are issued between the MFMAs of step k (spread, so
+//    the in-order issue never blocks on a full address FIFO), each with NST-1
+//    steps to land before the barrier that publishes it;
 //  * tile GEMM into register fragments: LDS -> VGPR fragments double-buffered
 //    across the K sub-steps (the reads of sub-step s+1 are in flight while
 //    the MFMAs of sub-step s run), 32x32 MFMAs accumulating in fp32 AGPRs;
@@ -68,26 +69,32 @@ __device__ __forceinline__ void load_lds_1k(i32x4_t r, uint8_t* dst, uint32_t vo
                  : "memory");
 }
 
+// wait until at most N of this wave's copies are outstanding (they retire in order)
+template <int N>
 __device__ __forceinline__ void wait_copies()
 {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int E, int O, int BM, int BN>
+template <int E, int O, int BM, int BN, int RB, int NST>
 __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
 {
     constexpr int EB = ElemInfo<E>::bytes;
-    constexpr int CE = 16 / EB;   // elements per 16-byte chunk
-    constexpr int KE = 128 / EB;  // K elements per step (128 bytes of a row)
+    constexpr int CE = 16 / EB;       // elements per 16-byte chunk
+    constexpr int KE = RB / EB;       // K elements per step
+    constexpr int CH = RB / 16;       // 16-byte chunks per staged row
+    constexpr int RPI = 1024 / RB;    // rows per copy instruction (64 lanes x 16 bytes)
+    constexpr int RSW = 256 / RB;     // rows per 256-byte line of the 64 LDS banks
     constexpr int TM = BM / 64, TN = BN / 64;
-    constexpr int AI = BM / 32, BI = BN / 32;  // LDS-DMA instructions per wave per step
-    constexpr int STAGE = (BM + BN) * 128;
-    constexpr int KSTEPS = (E == E_FP8) ? 2 : 4;
+    constexpr int AI = BM / (4 * RPI), BI = BN / (4 * RPI);  // copy instructions per wave per step
+    constexpr int STAGE = (BM + BN) * RB;
+    constexpr int KSTEPS = (E == E_FP8) ? RB / 64 : RB / 32;  // MFMAs along K per step
+    static_assert(KSTEPS >= 2 && KSTEPS % 2 == 0, "fragment slots alternate within a step");
+    static_assert(NST >= 2 && (NST - 2) * (AI + BI) + AI <= 63, "copies in flight");
     typedef typename Mfma32<E>::frag Frag;
-    typedef typename OutInfo<O>::T OutT;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases scalar
@@ -104,27 +111,31 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
     const i32x4_t rb = make_rsrc(p.B + n0 * (int64_t)ldbb);
     const int64_t KT = (K + KE - 1) / KE;  // K is a multiple of CE on this path
 
-    // ---- source offsets of the LDS-DMA instructions
-    // Wave w fills rows [w*BM/4, (w+1)*BM/4) of the A stage (and likewise of
-    // B), 8 rows per instruction.  Lane i lands at physical chunk i%8 of row
-    // i/8 of the instruction's 8 rows.  Rows are swizzled with row_swz(): a
-    // row's logical chunk c sits at physical chunk c ^ ((row/2) % 8), so the
-    // swizzle is applied on the source side: lane i loads logical chunk
-    // (i%8) ^ ((row/2) % 8), which for the rows of instruction j is
-    // (i%8) ^ ((4j + (i/8)/2) % 8) -- one value for even j, one for odd j.
+    // ---- staged layout: row r of a stage operand holds RB bytes of K as CH
+    // 16-byte chunks; logical chunk c sits at physical chunk c ^ swz(r), with
+    // swz(r) = (r / RSW) % CH, so the 16 lanes that read one chunk column
+    // from 16 consecutive rows cover all 64 banks.
+    //
+    // ---- copy instructions: wave w fills rows [w*BM/4, (w+1)*BM/4) of the A
+    // stage (likewise B), RPI rows per instruction; lane i lands at physical
+    // chunk i%CH of row i/CH, so it loads logical chunk (i%CH) ^ swz(row):
+    // the swizzle is applied on the source side.  For instruction j that is
+    // (i%CH) ^ ((4j + (i/CH)/RSW) % CH): one value for even j, one for odd j.
     // The per-lane part of the offset is fixed; the step's K offset and the
-    // instruction's 8-row block go into the scalar offset.  Rows past M or N:
+    // instruction's row block go into the scalar offset.  Rows past M or N:
     // on edge tiles their lanes read through an out-of-range offset (zeros);
     // they only feed outputs that are never stored.
-    const uint32_t lrow8 = lane >> 3;
-    const uint32_t lchunk0 = (lane & 7u) ^ (lrow8 >> 1);
-    const uint32_t lchunk1 = (lane & 7u) ^ (4u + (lrow8 >> 1));
-    const uint32_t va0 = (wave * (BM / 4) + lrow8) * ldab + lchunk0 * 16u;
-    const uint32_t va1 = (wave * (BM / 4) + lrow8) * ldab + lchunk1 * 16u;
-    const uint32_t vb0 = (wave * (BN / 4) + lrow8) * ldbb + lchunk0 * 16u;
-    const uint32_t vb1 = (wave * (BN / 4) + lrow8) * ldbb + lchunk1 * 16u;
+    const uint32_t lrowi = lane / CH;
+    const uint32_t lchunk0 = (lane % CH) ^ ((lrowi / RSW) % CH);
+    const uint32_t lchunk1 = (lane % CH) ^ ((4u + lrowi / RSW) % CH);
+    const uint32_t va0 = (wave * (BM / 4) + lrowi) * ldab + lchunk0 * 16u;
+    const uint32_t va1 = (wave * (BM / 4) + lrowi) * ldab + lchunk1 * 16u;
+    const uint32_t vb0 = (wave * (BN / 4) + lrowi) * ldbb + lchunk0 * 16u;
+    const uint32_t vb1 = (wave * (BN / 4) + lrowi) * ldbb + lchunk1 * 16u;
 
-    // copy instruction j (of AI) of operand A, or of BI of operand B, for K step kt into stage `st`
+    auto stage_ptr = [&](int64_t kt) __attribute__((always_inline)) -> uint8_t* {
+        return lds + (uint32_t)(kt % NST) * STAGE;
+    };
     auto chunk_oob = [&](int64_t kt, uint32_t lchunk) __attribute__((always_inline)) -> uint32_t {
         // a chunk at or past K (only in the last step) reads through an
         // out-of-range offset (bit 31 set): zeros.  Valid offsets stay below 2^31.
@@ -132,30 +143,32 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
         const uint32_t kmax = kleft >= KE ? (uint32_t)KE : (uint32_t)kleft;
         return (lchunk * CE < kmax) ? 0u : kOutOfRange;
     };
-    // a copy for a step past the last one reads through the out-of-range offset:
-    // it only writes zeros into a buffer that is not read again
-    auto copy_a = [&](auto edge, int64_t kt, uint8_t* st, int j) __attribute__((always_inline)) {
+    // copy instruction j of operand A (or B) for K step kt into its stage; a
+    // step past the last one reads through the out-of-range offset, which only
+    // writes zeros into a stage buffer that is not read again
+    auto copy_a = [&](auto edge, int64_t kt, int j) __attribute__((always_inline)) {
         uint32_t v = (j & 1) ? (va1 | chunk_oob(kt, lchunk1)) : (va0 | chunk_oob(kt, lchunk0));
         v |= kt < KT ? 0u : kOutOfRange;
         if constexpr (decltype(edge)::value)
-            v |= (int32_t)(wave * (BM / 4) + 8 * j + lrow8) < rows_a ? 0u : kOutOfRange;
-        load_lds_1k(ra, st + wave * (BM / 4) * 128 + j * 1024, v, (uint32_t)kt * 128u + (uint32_t)(8 * j) * ldab);
+            v |= (int32_t)(wave * (BM / 4) + RPI * j + lrowi) < rows_a ? 0u : kOutOfRange;
+        load_lds_1k(ra, stage_ptr(kt) + wave * (BM / 4) * RB + j * 1024, v,
+                    (uint32_t)kt * RB + (uint32_t)(RPI * j) * ldab);
     };
-    auto copy_b = [&](auto edge, int64_t kt, uint8_t* st, int j) __attribute__((always_inline)) {
+    auto copy_b = [&](auto edge, int64_t kt, int j) __attribute__((always_inline)) {
         uint32_t v = (j & 1) ? (vb1 | chunk_oob(kt, lchunk1)) : (vb0 | chunk_oob(kt, lchunk0));
         v |= kt < KT ? 0u : kOutOfRange;
         if constexpr (decltype(edge)::value)
-            v |= (int32_t)(wave * (BN / 4) + 8 * j + lrow8) < rows_b ? 0u : kOutOfRange;
-        load_lds_1k(rb, st + BM * 128 + wave * (BN / 4) * 128 + j * 1024, v,
-                    (uint32_t)kt * 128u + (uint32_t)(8 * j) * ldbb);
+            v |= (int32_t)(wave * (BN / 4) + RPI * j + lrowi) < rows_b ? 0u : kOutOfRange;
+        load_lds_1k(rb, stage_ptr(kt) + BM * RB + wave * (BN / 4) * RB + j * 1024, v,
+                    (uint32_t)kt * RB + (uint32_t)(RPI * j) * ldbb);
     };
 
-    // ---- fragment reads: every fragment row of this lane has the same (row/2)%8
+    // ---- fragment reads: every fragment row of this lane has the same swz(row)
     const uint32_t wm = wave >> 1, wn = wave & 1u;
     const uint32_t lrow = lane & 31u, lgrp = lane >> 5;
-    const uint32_t sw = (lrow >> 1) & 7u;
-    const uint32_t a_row0 = (wm * (BM / 2) + lrow) * 128u;
-    const uint32_t b_row0 = BM * 128u + (wn * (BN / 2) + lrow) * 128u;
+    const uint32_t sw = (lrow / RSW) % CH;
+    const uint32_t a_row0 = (wm * (BM / 2) + lrow) * RB;
+    const uint32_t b_row0 = BM * RB + (wn * (BN / 2) + lrow) * RB;
 
     Frag fa[2][TM], fb[2][TN];
     auto read_frags = [&](const uint8_t* st, int s, int slot) __attribute__((always_inline)) {
@@ -163,24 +176,24 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
         for (int i = 0; i < TM; ++i) {
             if constexpr (E == E_FP8) {
                 const uint32_t c0 = (uint32_t)(4 * s) + 2u * lgrp;
-                const u32x4 lo = lds128(st, a_row0 + i * 32 * 128 + ((c0 ^ sw) << 4));
-                const u32x4 hi = lds128(st, a_row0 + i * 32 * 128 + (((c0 + 1u) ^ sw) << 4));
+                const u32x4 lo = lds128(st, a_row0 + i * 32 * RB + ((c0 ^ sw) << 4));
+                const u32x4 hi = lds128(st, a_row0 + i * 32 * RB + (((c0 + 1u) ^ sw) << 4));
                 fa[slot][i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
             } else {
-                fa[slot][i] = lds128(st, a_row0 + i * 32 * 128 + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
+                fa[slot][i] = lds128(st, a_row0 + i * 32 * RB + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
             }
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             if constexpr (E == E_FP8) {
                 const uint32_t c0 = (uint32_t)(4 * s) + 2u * lgrp;
-                const u32x4 lo = lds128(st, b_row0 + j * 32 * 128 + ((c0 ^ sw) << 4));
-                const u32x4 hi = lds128(st, b_row0 + j * 32 * 128 + (((c0 + 1u) ^ sw) << 4));
+                const u32x4 lo = lds128(st, b_row0 + j * 32 * RB + ((c0 ^ sw) << 4));
+                const u32x4 hi = lds128(st, b_row0 + j * 32 * RB + (((c0 + 1u) ^ sw) << 4));
                 fb[slot][j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
             } else {
-                fb[slot][j] = lds128(st, b_row0 + j * 32 * 128 + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
+                fb[slot][j] = lds128(st, b_row0 + j * 32 * RB + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
             }
         }
     };
@@ -218,50 +231,53 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
     };
     auto nothing = [](int) {};
 
-    // One K step out of `cur`.  Entering, the fragments of its sub-step 0 are
-    // in slot 0 and the A copies of step kt+1 (into `nxt`) are in flight; the
-    // B copies of step kt+1 are issued between the sub-step-0 MFMAs.  After the
-    // barrier, the A copies of step kt+2 (into `cur`, now free) go out between
-    // the last sub-step's MFMAs, and the first fragments of step kt+1 are read
-    // (harmlessly, from a stale buffer, after the last step).
-    auto step = [&](auto edge, int64_t kt, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+    // One K step out of stage kt % NST.  Entering, the fragments of its
+    // sub-step 0 are in slot 0.  The B copies of step kt+NST-1 go out between
+    // the sub-step-0 MFMAs (their stage was freed by the previous barrier).
+    // The barrier before the last sub-step publishes step kt+1 (copies of
+    // steps past kt+1 may still be in flight) and frees stage kt % NST: the A
+    // copies of step kt+NST go out between the last sub-step's MFMAs, while
+    // the first fragments of step kt+1 are read.
+    auto step = [&](auto edge, int64_t kt) __attribute__((always_inline)) {
+        const uint8_t* cur = stage_ptr(kt);
 #pragma unroll
         for (int s = 0; s < KSTEPS - 1; ++s) {
             read_frags(cur, s + 1, (s + 1) & 1);
             if (s == 0)
-                mma(s & 1, [&](int q) __attribute__((always_inline)) { copy_b(edge, kt + 1, nxt, q); },
+                mma(s & 1, [&](int q) __attribute__((always_inline)) { copy_b(edge, kt + NST - 1, q); },
                     std::integral_constant<int, BI>{});
             else
                 mma(s & 1, nothing, std::integral_constant<int, 0>{});
         }
         __builtin_amdgcn_sched_barrier(0);
-        wait_copies();    // own copies of step kt+1 landed ...
-        __syncthreads();  // ... and every wave's; every wave is done reading `cur`
+        wait_copies<(NST - 2) * (AI + BI)>();  // own copies of step kt+1 landed ...
+        __syncthreads();                        // ... and every wave's; stage kt % NST is free
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(nxt, 0, 0);
-        mma((KSTEPS - 1) & 1, [&](int q) __attribute__((always_inline)) { copy_a(edge, kt + 2, cur, q); },
+        read_frags(stage_ptr(kt + 1), 0, 0);   // (stale, unused, after the last step)
+        mma((KSTEPS - 1) & 1, [&](int q) __attribute__((always_inline)) { copy_a(edge, kt + NST, q); },
             std::integral_constant<int, AI>{});
     };
 
     auto run = [&](auto edge) __attribute__((always_inline)) {
+        // steps 0 .. NST-2 complete, plus the A half of step NST-1
 #pragma unroll
-        for (int j = 0; j < AI; ++j)
-            copy_a(edge, 0, lds0, j);
+        for (int st = 0; st < NST - 1; ++st) {
 #pragma unroll
-        for (int j = 0; j < BI; ++j)
-            copy_b(edge, 0, lds0, j);
+            for (int j = 0; j < AI; ++j)
+                copy_a(edge, st, j);
 #pragma unroll
-        for (int j = 0; j < AI; ++j)
-            copy_a(edge, 1, lds1, j);
-        wait_copies();
-        __syncthreads();
-        read_frags(lds0, 0, 0);
-        for (int64_t kt = 0; kt < KT; kt += 2) {
-            step(edge, kt, lds0, lds1);
-            if (kt + 1 < KT)
-                step(edge, kt + 1, lds1, lds0);
+            for (int j = 0; j < BI; ++j)
+                copy_b(edge, st, j);
         }
-        wait_copies();  // copies past the last step (zeros) must land before LDS is reused
+#pragma unroll
+        for (int j = 0; j < AI; ++j)
+            copy_a(edge, NST - 1, j);
+        wait_copies<(NST - 2) * (AI + BI) + AI>();  // step 0 landed
+        __syncthreads();
+        read_frags(stage_ptr(0), 0, 0);
+        for (int64_t kt = 0; kt < KT; ++kt)
+            step(edge, kt);
+        wait_copies<0>();  // copies past the last step (zeros) must land before LDS is reused
     };
     if (KT > 0) {
         if (rows_a == BM && rows_b == BN)
@@ -310,13 +326,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
         // 16-bit output: each wave stages its sub-tile in its own LDS region
         // (row-major, 16-byte chunks XOR-swizzled by row), then writes whole
         // rows with 16-byte stores.
-        constexpr int RB = WC * 2;       // bytes per staged row
-        constexpr int NCH = RB / 16;     // 16-byte chunks per row
-        constexpr int WBYTES = WR * RB;  // bytes per wave
-        constexpr int WPS = STAGE / WBYTES;  // waves per stage array
-        static_assert(2 * WPS >= 4, "epilogue staging must fit the two stage arrays");
+        constexpr int OB = WC * 2;          // bytes per staged output row
+        constexpr int NCH = OB / 16;        // 16-byte chunks per row
+        constexpr int WBYTES = WR * OB;     // bytes per wave
+        static_assert(4 * WBYTES <= NST * STAGE, "epilogue staging must fit the stage buffers");
         __syncthreads();  // every wave is done reading the stage buffers
-        uint8_t* ep = (wave / WPS ? lds1 : lds0) + (wave % WPS) * WBYTES;
+        uint8_t* ep = lds + wave * WBYTES;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const uint32_t r = i * 32 + lrow;
@@ -329,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
                                         ((uint32_t)convert_out<O>(out_val(i, j, 4 * g + 1)) << 16);
                     const uint32_t hi = (uint32_t)convert_out<O>(out_val(i, j, 4 * g + 2)) |
                                         ((uint32_t)convert_out<O>(out_val(i, j, 4 * g + 3)) << 16);
-                    *(u32x2*)(ep + r * RB + ((c ^ (r % NCH)) << 4) + lgrp * 8) = u32x2{lo, hi};
+                    *(u32x2*)(ep + r * OB + ((c ^ (r % NCH)) << 4) + lgrp * 8) = u32x2{lo, hi};
                 }
             }
         }
@@ -339,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
         for (int t = 0; t < WR * NCH / 64; ++t) {
             const uint32_t idx = t * 64 + lane;
             const uint32_t r = idx / NCH, c = idx % NCH;
-            const u32x4 q = lds128(ep, r * RB + ((c ^ (r % NCH)) << 4));
+            const u32x4 q = lds128(ep, r * OB + ((c ^ (r % NCH)) << 4));
             const int64_t row = wrow0 + r, col = wcol0 + c * 8;
             if (row < M) {
                 if (col + 8 <= N) {

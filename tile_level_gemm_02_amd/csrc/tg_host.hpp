@@ -105,13 +105,17 @@ inline bool nt_eligible(const TileArgs& a)
     return (a.K % (16 / EB)) == 0 && 256 * a.lda * EB + a.K * EB < lim && 256 * a.ldb * EB + a.K * EB < lim;
 }
 
+// Staging depth of the NT kernel: bytes of K per staged row and number of stages.
+template <int E> struct NtStaging { static constexpr int RB = 128, NST = 2; };
+
 template <int E, int O, int BM, int BN>
 tg_status launch_nt(const TileArgs& a, hipStream_t s)
 {
     const int64_t tiles = n_tiles<BM, BN>(a.M, a.N);
     if (tiles > 0x7FFFFFFF)
         return TG_ERR_NOT_SUPPORTED;
-    hipLaunchKernelGGL((gemm_nt<E, O, BM, BN>), dim3((uint32_t)tiles), dim3(kThreads), 0, s, a);
+    constexpr int RB = NtStaging<E>::RB, NST = NtStaging<E>::NST;
+    hipLaunchKernelGGL((gemm_nt<E, O, BM, BN, RB, NST>), dim3((uint32_t)tiles), dim3(kThreads), 0, s, a);
     return launched();
 }
 
