@@ -15,7 +15,7 @@ each launch inside the timed region), `cpu_baseline` (the CPU oracle timed
 on a bounded sample of the same workload) and `secondary` (the skinny M=16
 GEMM's GB/s against the HBM peak, the fp8 and w4a16 workloads), each
 secondary timed launch by launch with the 256 MB Infinity Cache flushed
-before every launch.
+(by a 512 MiB read) before every launch.
 """
 from __future__ import annotations
 
@@ -85,10 +85,16 @@ def median(xs):
 
 
 def make_flush():
+    """Evict the Infinity Cache by READING 512 MiB (twice its size).
+
+    A write-based flush would leave ~256 MB of dirty lines whose write-back
+    then competes with the next kernel's reads (measured: it halves the read
+    bandwidth a streaming kernel sees right after it)."""
     import torch
 
-    buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-    return lambda: buf.fill_(1.0)
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    return lambda: torch.sum(buf, dim=0, out=out)
 
 
 # ------------------------------------------------------------------ workloads

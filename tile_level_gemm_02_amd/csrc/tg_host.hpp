@@ -163,18 +163,19 @@ tg_status gemm_16bit(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     hipStream_t s = (hipStream_t)stream;
     if (M <= 16 && b_layout == TG_COL_MAJOR && K > 0) {
         SkinnyArgs sa{M, N, K, (const uint8_t*)A, lda, (const uint8_t*)B, ldb, C, ldc};
-        const int64_t blocks = (N + 15) / 16;
+        constexpr int NT = 2, UNR = 8;
+        const int64_t blocks = (N + 16 * NT - 1) / (16 * NT);
         if (blocks > 0x7FFFFFFF)
             return TG_ERR_NOT_SUPPORTED;
         switch (c_dtype) {
         case TG_F32:
-            hipLaunchKernelGGL((skinny_gemm<E, O_F32, 8, 8>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
+            hipLaunchKernelGGL((skinny_gemm<E, O_F32, 8, NT, UNR>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
             break;
         case TG_F16:
-            hipLaunchKernelGGL((skinny_gemm<E, O_F16, 8, 8>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
+            hipLaunchKernelGGL((skinny_gemm<E, O_F16, 8, NT, UNR>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
             break;
         default:
-            hipLaunchKernelGGL((skinny_gemm<E, O_BF16, 8, 8>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
+            hipLaunchKernelGGL((skinny_gemm<E, O_BF16, 8, NT, UNR>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
             break;
         }
         return launched();

@@ -286,12 +286,14 @@ __global__ __launch_bounds__(kThreads) void tile_gemm(TileArgs p)
 }
 
 // --------------------------------------------------------------------------
-// Skinny GEMM: M <= 16, B K-contiguous, 16-bit inputs.  A workgroup owns 16
-// output columns; its WAVES waves split K into contiguous ranges of 32-wide
-// blocks, each running 16x16x32 MFMAs on operands loaded straight from global
-// memory (lane l: row/column l%16, k offset 8*(l/16) within the block), UNROLL
-// blocks of loads in flight per wave.  The partial 16x16 tiles are summed
-// through LDS in a fixed wave order.
+// Skinny GEMM: M <= 16, B K-contiguous, 16-bit inputs.  A workgroup owns
+// 16*NT output columns; its WAVES waves split K into contiguous ranges of
+// 32-wide blocks, each running 16x16x32 MFMAs on operands loaded straight from
+// global memory (lane l: row/column l%16, k offset 8*(l/16) within the block).
+// One A fragment feeds NT column tiles, halving the A (L2) traffic per byte
+// of B at NT = 2; groups of UNR blocks are double-buffered so the next group's
+// loads are in flight during this group's MFMAs.  The partial 16x16 tiles are
+// summed through LDS in a fixed wave order (deterministic).
 // --------------------------------------------------------------------------
 struct SkinnyArgs {
     int64_t M, N, K;
@@ -317,60 +319,106 @@ template <> struct Mfma16<E_BF16> {
     }
 };
 
-template <int E, int O, int WAVES, int UNROLL>
+template <int E, int O, int WAVES, int NT, int UNR>
 __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
 {
     typedef typename OutInfo<O>::T OutT;
-    __shared__ float red[WAVES][4][64];
+    __shared__ float red[WAVES][NT][4][64];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t col = n0 + (lane & 15u);
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * NT);
     const int64_t row = lane & 15u;
-    const int64_t koff = (int64_t)(lane >> 4) * 8;
+    const int64_t koff = (int64_t)(lane >> 4) * 8;  // element offset inside a 32-wide K block
     const int64_t KB = (K + 31) / 32;
     const int64_t kb0 = KB * wave / WAVES, kb1 = KB * (wave + 1) / WAVES;
-    const bool col_ok = col < N, row_ok = row < M;
-    const uint8_t* bptr = p.B + col * p.ldb * 2;
-    const uint8_t* aptr = p.A + row * p.lda * 2;
+    const bool rok = row < M;
+    const uint8_t* aptr = p.A + (rok ? row : 0) * p.lda * 2;
+    bool cok[NT];
+    const uint8_t* bptr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int64_t col = n0 + 16 * t + (lane & 15u);
+        cok[t] = col < N;
+        bptr[t] = p.B + (cok[t] ? col : 0) * p.ldb * 2;
+    }
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t kb = kb0; kb < kb1; kb += UNROLL) {
-        u32x4 a[UNROLL], b[UNROLL];
+    // Each lane's A fragment (row l%16, 8 k) serves the NT column tiles.
+    f32x4 acc[NT];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int64_t k = (kb + u) * 32 + koff;
-            const bool in = (kb + u < kb1) && k < K;
-            u32x4 vb = {0u, 0u, 0u, 0u}, va = {0u, 0u, 0u, 0u};
-            if (in && col_ok)
-                vb = (k + 8 <= K) ? ldg128(bptr + k * 2) : load_chunk_partial<2>(bptr + k * 2, K - k);
-            if (in && row_ok)
-                va = (k + 8 <= K) ? ldg128(aptr + k * 2) : load_chunk_partial<2>(aptr + k * 2, K - k);
-            a[u] = va;
-            b[u] = vb;
+    for (int t = 0; t < NT; ++t)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 a0[UNR], a1[UNR], b0[UNR][NT], b1[UNR][NT];
+    auto load_group = [&](u32x4 (&a)[UNR], u32x4 (&b)[UNR][NT], int64_t kb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int64_t k = (kb + u) * 32 + koff;  // whole 16-byte chunks: the block is full
+            a[u] = rok ? ldg128(aptr + k * 2) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                b[u][t] = cok[t] ? ldg128(bptr[t] + k * 2) : u32x4{0u, 0u, 0u, 0u};
         }
+    };
+    auto mma_group = [&](u32x4 (&a)[UNR], u32x4 (&b)[UNR][NT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            acc = Mfma16<E>::run(a[u], b[u], acc);
+        for (int u = 0; u < UNR; ++u)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = Mfma16<E>::run(a[u], b[u][t], acc[t]);
+    };
+
+    // Whole blocks in groups of UNR, double-buffered: the loads of the next
+    // group are in flight while the MFMAs of this one run.
+    const int64_t kfull = K / 32 < kb1 ? K / 32 : kb1;  // blocks [kb0, kfull) hold no K tail
+    const int64_t ngroups = kfull > kb0 ? (kfull - kb0) / UNR : 0;
+    if (ngroups > 0) {
+        load_group(a0, b0, kb0);
+        for (int64_t g = 0; g < ngroups; g += 2) {
+            if (g + 1 < ngroups)
+                load_group(a1, b1, kb0 + (g + 1) * UNR);
+            mma_group(a0, b0);
+            if (g + 1 < ngroups) {
+                if (g + 2 < ngroups)
+                    load_group(a0, b0, kb0 + (g + 2) * UNR);
+                mma_group(a1, b1);
+            }
+        }
+    }
+    // remaining blocks of this wave, the K tail masked element by element
+    for (int64_t kb = kb0 + ngroups * UNR; kb < kb1; ++kb) {
+        const int64_t k = kb * 32 + koff;
+        u32x4 a = {0u, 0u, 0u, 0u};
+        if (rok && k < K)
+            a = (k + 8 <= K) ? ldg128(aptr + k * 2) : load_chunk_partial<2>(aptr + k * 2, K - k);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            u32x4 b = {0u, 0u, 0u, 0u};
+            if (cok[t] && k < K)
+                b = (k + 8 <= K) ? ldg128(bptr[t] + k * 2) : load_chunk_partial<2>(bptr[t] + k * 2, K - k);
+            acc[t] = Mfma16<E>::run(a, b, acc[t]);
+        }
     }
 
     mfma_drain();
-    // partial tile of this wave: value v of lane l is row 4*(l/16) + v, column l%16
+    // partial tiles of this wave: value v of lane l is row 4*(l/16) + v, column l%16
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-        red[wave][v][lane] = acc[v];
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            red[wave][t][v][lane] = acc[t][v];
     __syncthreads();
-    if (wave == 0) {
+    if (wave < NT) {  // wave t sums tile t over the K split, in wave order
+        const int t = (int)wave;
+        const int64_t col = n0 + 16 * t + (lane & 15u);
         OutT* C = (OutT*)p.C;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            float s = red[0][v][lane];
+            float s = red[0][t][v][lane];
 #pragma unroll
             for (int w = 1; w < WAVES; ++w)
-                s += red[w][v][lane];
+                s += red[w][t][v][lane];
             const int64_t r = (int64_t)(lane >> 4) * 4 + v;
-            if (r < M && col_ok)
+            if (r < M && col < N)
                 C[r * p.ldc + col] = convert_out<O>(s);
         }
     }
