@@ -192,6 +192,54 @@ def test_w4a16_small(tg, shape):
     assert ok, (r, idx)
 
 
+def _gpu_strided(t, extra):
+    """t copied to the GPU as a view whose row stride has `extra` more elements."""
+    buf = torch.zeros((t.shape[0], t.shape[1] + extra), dtype=t.dtype, device="cuda")
+    buf[:, : t.shape[1]] = t.cuda()
+    return buf[:, : t.shape[1]]
+
+
+# K a multiple of 256: the direct kernel (int4 words and scale pairs copied
+# straight to LDS); K steps not a multiple of the copy-ring depth, ragged M
+# and N tiles, a single row and column tile
+@pytest.mark.parametrize("shape", [(1, 8, 256), (65, 129, 768), (64, 128, 256), (9, 70, 2048),
+                                   (200, 384, 1280)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("zp", [0, 15])
+def test_w4a16_direct(tg, shape, zp):
+    M, N, K = shape
+    A, q, s = _w4_inputs(M, N, K, seed=M + 3 * N + zp)
+    C = _run_w4(tg, A, q, s, zp=zp)
+    cref, S = oracle.w4a16(A, q, s, K, zero_point=zp)
+    ok, r, idx = ochk.check(_f64(C), cref, S, K, "f16")
+    assert ok, (r, idx)
+
+
+# row strides above the minimum on every operand (even scale stride: direct
+# kernel), then an odd scale stride and 2-byte-aligned scales (fallback kernel)
+@pytest.mark.parametrize("case", ["strided", "odd_lds", "scales_2b_aligned"])
+def test_w4a16_layouts(tg, case):
+    M, N, K = 70, 136, 512
+    A, q, s = _w4_inputs(M, N, K, seed=41)
+    Ad, qd, sd = A.cuda(), q.cuda(), s.cuda()
+    if case == "strided":
+        Ad, qd, sd = _gpu_strided(A, 24), _gpu_strided(q, 4), _gpu_strided(s, 2)
+        assert Ad.stride(0) == K + 24 and qd.stride(0) == K // 8 + 4 and sd.stride(0) == K // 128 + 2
+    elif case == "odd_lds":
+        sd = _gpu_strided(s, 1)
+        assert sd.stride(0) % 2 == 1
+    else:
+        big = torch.zeros(s.numel() + 1, dtype=torch.float16, device="cuda")
+        big[1:] = s.reshape(-1).cuda()
+        sd = big[1:].view(N, K // 128)
+        assert sd.data_ptr() % 4 == 2
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    tg.tg_gemm_w4a16(Ad, qd, sd, C)
+    torch.cuda.synchronize()
+    cref, S = oracle.w4a16(A, q, s, K)
+    ok, r, idx = ochk.check(_f64(C), cref, S, K, "f16")
+    assert ok, (case, r, idx)
+
+
 @pytest.mark.parametrize("zp", [0, 8, 15])
 def test_dequant_bit_exact(tg, zp):
     N, K = 300, 1024

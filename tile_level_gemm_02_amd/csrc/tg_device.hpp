@@ -152,31 +152,41 @@ __device__ __forceinline__ u32x4 lds128(const uint8_t* lds, uint32_t off)
 
 // ------------------------------------------------------------ int4 dequant
 // Eight int4 weights of one 32-bit word -> eight fp16 values, in k order
-// (nibble j, bits 4j..4j+3, is k offset j).  Each nibble q is placed in the
-// fraction of the fp16 number 1024 + q (bits 0x6400 | q), the exact integer
-// (1024 + zero_point) is subtracted (exact: |q - zp| <= 15), and the result
-// is multiplied by the fp16 scale with one round-to-nearest-even step, which
-// is fp16_RNE((q - zp) * s).  Packed-half arithmetic, two weights per op.
-__device__ __forceinline__ u32x4 dequant_w4_word(uint32_t w, f16x2 zp_bias, f16x2 s2)
+// (nibble j, bits 4j..4j+3, is k offset j), W = fp16_RNE((q - zp) * s).
+// Per byte (two nibbles, k offsets 2j and 2j+1):
+//   t = [byte j, 0, byte j, 0]                      (one byte permute)
+//   x = (t & 0x00F0000F) | 0x64006400               (one and-or)
+//     low half  = fp16 1024 + q_lo    (q in the fraction's low bits)
+//     high half = fp16 1024 + 16*q_hi (q four bits up)
+//   h = x * (1, 1/16) + (-(1024+zp), -(64+zp))      (packed fma: exact, the
+//     result q - zp is a small integer)
+//   w = h * (s, s)                                  (packed multiply: the one
+//     round-to-nearest-even step)
+struct W4Consts {
+    f16x2 mul;   // (1, 1/16)
+    f16x2 bias;  // (-(1024 + zp), -(64 + zp))
+};
+
+__device__ __forceinline__ W4Consts w4_consts(int zero_point)
+{
+    W4Consts c;
+    c.mul = f16x2{(_Float16)1.0f, (_Float16)0.0625f};
+    c.bias = f16x2{(_Float16)(-(1024 + zero_point)), (_Float16)(-(64 + zero_point))};  // exact
+    return c;
+}
+
+__device__ __forceinline__ u32x4 dequant_w4_word(uint32_t w, W4Consts c, f16x2 s2)
 {
     uint32_t out[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        uint32_t lo = (w >> (8 * j)) & 0xFu;
-        uint32_t hi = (w >> (8 * j + 4)) & 0xFu;
-        uint32_t x = lo | (hi << 16) | 0x64006400u;
-        f16x2 h = bit_cast<f16x2>(x);
-        h = h - zp_bias;
-        h = h * s2;
-        out[j] = bit_cast<uint32_t>(h);
+        const uint32_t sel = 0x0C000C00u | ((uint32_t)j << 16) | (uint32_t)j;
+        const uint32_t t = __builtin_amdgcn_perm(0u, w, sel);
+        const uint32_t x = (t & 0x00F0000Fu) | 0x64006400u;
+        const f16x2 h = __builtin_elementwise_fma(bit_cast<f16x2>(x), c.mul, c.bias);
+        out[j] = bit_cast<uint32_t>(h * s2);
     }
     return u32x4{out[0], out[1], out[2], out[3]};
-}
-
-__device__ __forceinline__ f16x2 w4_zero_bias(int zero_point)
-{
-    _Float16 b = (_Float16)(1024 + zero_point);  // exact
-    return f16x2{b, b};
 }
 
 // ------------------------------------------------------- tile scheduling

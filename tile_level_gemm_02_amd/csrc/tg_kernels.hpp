@@ -157,12 +157,12 @@ __global__ __launch_bounds__(kThreads) void tile_gemm(TileArgs p)
             sts128(As, swz(idx >> 3, idx & 7u), ra[i]);
         }
         if constexpr (W4) {
-            const f16x2 bias = w4_zero_bias(p.zero_point);
+            const W4Consts wc = w4_consts(p.zero_point);
 #pragma unroll
             for (int i = 0; i < B_CH; ++i) {
                 const uint32_t idx = tid + kThreads * i;
                 const _Float16 s = bit_cast<_Float16>(rs[i]);
-                sts128(Bs, swz(idx >> 3, idx & 7u), dequant_w4_word(rq[i], bias, f16x2{s, s}));
+                sts128(Bs, swz(idx >> 3, idx & 7u), dequant_w4_word(rq[i], wc, f16x2{s, s}));
             }
         } else if constexpr (BL == B_KCONTIG) {
 #pragma unroll

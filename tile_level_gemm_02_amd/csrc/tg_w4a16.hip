@@ -1,6 +1,7 @@
 // tg_gemm_w4a16 and tg_dequant_w4 (contract in include/tg.h).  Both run the
 // same device routine, tg::dequant_w4_word, so the GEMM's weights are
 // bit-identical to what tg_dequant_w4 writes.
+#include "tg_gemm_w4.hpp"
 #include "tg_host.hpp"
 
 namespace tg {
@@ -9,12 +10,12 @@ __global__ __launch_bounds__(256) void dequant_w4_kernel(DequantArgs p)
 {
     const int64_t words = p.K / 8;
     const int64_t total = p.N * words;
-    const f16x2 bias = w4_zero_bias(p.zero_point);
+    const W4Consts wc = w4_consts(p.zero_point);
     for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256) {
         const int64_t n = t / words, w = t - n * words;
         const uint32_t q = p.qw[n * p.ldq + w];
         const _Float16 s = bit_cast<_Float16>(p.scales[n * p.lds + (w * 8) / p.group_size]);
-        *(u32x4*)(p.W + n * p.ldw + w * 8) = dequant_w4_word(q, bias, f16x2{s, s});
+        *(u32x4*)(p.W + n * p.ldw + w * 8) = dequant_w4_word(q, wc, f16x2{s, s});
     }
 }
 
@@ -38,6 +39,21 @@ tg_status check_w4(int64_t N, int64_t K, const int32_t* qweight, int64_t ldq, co
             return TG_ERR_MISALIGNED;
     }
     return TG_OK;
+}
+
+// gemm_w4 takes K in whole pairs of scale groups (it fetches a column's two
+// scales of 256 K as one aligned 4-byte word) and addresses each operand
+// through a buffer resource of kNumRecords bytes based at its tile's first
+// row: every offset it forms, including the out-of-range marker added to
+// one, must stay below 2^32.
+bool w4_direct_eligible(const tg::TileArgs& a)
+{
+    if (a.K % 256 != 0 || ((uintptr_t)a.scales & 3u) != 0 || (a.lds & 1) != 0)
+        return false;
+    const int64_t lim = (int64_t)tg::kNumRecords;
+    const int64_t kpast = a.K + 16 * 64;  // steps issued past the last one
+    return 64 * a.lda * 2 + kpast * 2 < lim && 128 * a.ldq * 4 + kpast / 2 < lim &&
+           128 * a.lds * 2 + kpast / 32 < lim;
 }
 
 }  // namespace
@@ -80,6 +96,14 @@ extern "C" tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* 
     a.lds = lds;
     a.zero_point = zero_point;
     hipStream_t s = (hipStream_t)stream;
+    if (w4_direct_eligible(a)) {
+        constexpr int BM = 64, BN = 128, NA = 6;
+        const int64_t tiles = tg::n_tiles<BM, BN>(M, N);
+        if (tiles > 0x7FFFFFFF)
+            return TG_ERR_NOT_SUPPORTED;
+        hipLaunchKernelGGL((tg::gemm_w4<BM, BN, NA>), dim3((uint32_t)tiles), dim3(tg::kThreads), 0, s, a);
+        return tg::launched();
+    }
     if (tg::n_tiles<128, 128>(M, N) >= 96)
         return tg::launch_tile<tg::E_F16, tg::B_KCONTIG, tg::O_F16, 128, 128, true>(a, s);
     return tg::launch_tile<tg::E_F16, tg::B_KCONTIG, tg::O_F16, 64, 64, true>(a, s);
