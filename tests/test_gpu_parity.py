@@ -199,11 +199,13 @@ def _gpu_strided(t, extra):
     return buf[:, : t.shape[1]]
 
 
-# K a multiple of 256: the direct kernel (int4 words and scale pairs copied
-# straight to LDS); K steps not a multiple of the copy-ring depth, ragged M
-# and N tiles, a single row and column tile
+# K a multiple of 256 up to 16384: the direct kernel (int4 words and scales
+# copied straight to LDS); K steps not a multiple of the copy-ring depth,
+# ragged M and N tiles, a single row and column tile, the largest K with all
+# scales held in LDS, and one K beyond it (register-staged kernel)
 @pytest.mark.parametrize("shape", [(1, 8, 256), (65, 129, 768), (64, 128, 256), (9, 70, 2048),
-                                   (200, 384, 1280)], ids=lambda s: "x".join(map(str, s)))
+                                   (200, 384, 1280), (64, 256, 16384), (16, 64, 16640)],
+                         ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("zp", [0, 15])
 def test_w4a16_direct(tg, shape, zp):
     M, N, K = shape

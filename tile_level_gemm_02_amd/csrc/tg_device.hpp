@@ -163,8 +163,9 @@ __device__ __forceinline__ u32x4 lds128(const uint8_t* lds, uint32_t off)
 //   w = h * (s, s)                                  (packed multiply: the one
 //     round-to-nearest-even step)
 struct W4Consts {
-    f16x2 mul;   // (1, 1/16)
-    f16x2 bias;  // (-(1024 + zp), -(64 + zp))
+    f16x2 mul;      // (1, 1/16)
+    f16x2 bias;     // (-(1024 + zp), -(64 + zp))
+    uint32_t mask;  // 0x00F0000F, held in a vector register
 };
 
 __device__ __forceinline__ W4Consts w4_consts(int zero_point)
@@ -172,6 +173,9 @@ __device__ __forceinline__ W4Consts w4_consts(int zero_point)
     W4Consts c;
     c.mul = f16x2{(_Float16)1.0f, (_Float16)0.0625f};
     c.bias = f16x2{(_Float16)(-(1024 + zero_point)), (_Float16)(-(64 + zero_point))};  // exact
+    // in a register, so the and-or below is one instruction (its three-operand
+    // form takes no literal and at most one scalar operand)
+    asm("v_mov_b32 %0, 0x00F0000F" : "=v"(c.mask));
     return c;
 }
 
@@ -182,7 +186,8 @@ __device__ __forceinline__ u32x4 dequant_w4_word(uint32_t w, W4Consts c, f16x2 s
     for (int j = 0; j < 4; ++j) {
         const uint32_t sel = 0x0C000C00u | ((uint32_t)j << 16) | (uint32_t)j;
         const uint32_t t = __builtin_amdgcn_perm(0u, w, sel);
-        const uint32_t x = (t & 0x00F0000Fu) | 0x64006400u;
+        uint32_t x;  // (t & 0x00F0000F) | 0x64006400
+        asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(x) : "v"(t), "v"(c.mask), "s"(0x64006400u));
         const f16x2 h = __builtin_elementwise_fma(bit_cast<f16x2>(x), c.mul, c.bias);
         out[j] = bit_cast<uint32_t>(h * s2);
     }

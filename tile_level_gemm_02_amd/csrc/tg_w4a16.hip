@@ -41,19 +41,20 @@ tg_status check_w4(int64_t N, int64_t K, const int32_t* qweight, int64_t ldq, co
     return TG_OK;
 }
 
-// gemm_w4 takes K in whole pairs of scale groups (it fetches a column's two
-// scales of 256 K as one aligned 4-byte word) and addresses each operand
-// through a buffer resource of kNumRecords bytes based at its tile's first
-// row: every offset it forms, including the out-of-range marker added to
-// one, must stay below 2^32.
+// gemm_w4 takes K in whole pairs of scale groups, up to its LDS capacity for
+// scales (it fetches a column's scales as aligned 4-byte pairs), and
+// addresses each operand through a buffer resource of kNumRecords bytes based
+// at its tile's first row: every offset it forms, including the out-of-range
+// marker added to one, must stay below 2^32.
 bool w4_direct_eligible(const tg::TileArgs& a)
 {
-    if (a.K % 256 != 0 || ((uintptr_t)a.scales & 3u) != 0 || (a.lds & 1) != 0)
+    if (a.K % 256 != 0 || a.K > 128 * tg::kW4MaxGroups || ((uintptr_t)a.scales & 3u) != 0 ||
+        (a.lds & 1) != 0)
         return false;
     const int64_t lim = (int64_t)tg::kNumRecords;
-    const int64_t kpast = a.K + 16 * 64;  // steps issued past the last one
+    const int64_t kpast = a.K + 16 * 128;  // with the steps issued past the last one
     return 64 * a.lda * 2 + kpast * 2 < lim && 128 * a.ldq * 4 + kpast / 2 < lim &&
-           128 * a.lds * 2 + kpast / 32 < lim;
+           128 * a.lds * 2 + a.K / 64 < lim;
 }
 
 }  // namespace
@@ -97,11 +98,11 @@ extern "C" tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* 
     a.zero_point = zero_point;
     hipStream_t s = (hipStream_t)stream;
     if (w4_direct_eligible(a)) {
-        constexpr int BM = 64, BN = 128, NA = 6;
+        constexpr int BM = 64, BN = 128, NA = 4;
         const int64_t tiles = tg::n_tiles<BM, BN>(M, N);
         if (tiles > 0x7FFFFFFF)
             return TG_ERR_NOT_SUPPORTED;
-        hipLaunchKernelGGL((tg::gemm_w4<BM, BN, NA>), dim3((uint32_t)tiles), dim3(tg::kThreads), 0, s, a);
+        hipLaunchKernelGGL((tg::gemm_w4<BM, NA>), dim3((uint32_t)tiles), dim3(tg::kThreads), 0, s, a);
         return tg::launched();
     }
     if (tg::n_tiles<128, 128>(M, N) >= 96)
