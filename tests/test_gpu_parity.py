@@ -132,6 +132,18 @@ def test_medium_multi_tile(tg, dt, lay):
         _check(C, A, B, dt, lay, "f32", sa, sb, rows=rows)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+@pytest.mark.parametrize("out", ["f16", "bf16"])
+def test_large_ragged_16bit_out(tg, dt, out):
+    """The 256 x 256 tile (8 waves) with a 16-bit output staged through LDS; N % 8 != 0
+    exercises the partial 16-byte store at the right edge."""
+    M, N, K = 3600, 3404, 272  # K a multiple of 16: the NT kernel for fp8 too
+    A, B, sa, sb = _inputs(dt, M, N, K, "col", seed=N + K)
+    C = _run_dense(tg, dt, A, B, "col", out, scale_a=sa, scale_b=sb)
+    rows = np.r_[0:24, 1800:1824, M - 24 : M]
+    _check(C, A, B, dt, "col", out, sa, sb, rows=rows)
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16", "fp8"])
 def test_exact_structure(tg, dt):
     """Identity and all-ones inputs have exactly representable results: bit-exact."""

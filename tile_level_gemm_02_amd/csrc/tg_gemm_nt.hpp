@@ -77,8 +77,11 @@ __device__ __forceinline__ void wait_copies()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int E, int O, int BM, int BN, int RB, int NST>
-__global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
+// WM x WN waves share the tile (each computes a BM/WM x BN/WN sub-tile).
+// With 8 waves (two per SIMD) the LDS sustains about twice the fragment-read
+// rate of 4 waves (one per SIMD), which the 256 x 256 tile needs.
+template <int E, int O, int BM, int BN, int RB, int NST, int WM = 2, int WN = 2>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
 {
     constexpr int EB = ElemInfo<E>::bytes;
     constexpr int CE = 16 / EB;       // elements per 16-byte chunk
@@ -86,8 +89,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
     constexpr int CH = RB / 16;       // 16-byte chunks per staged row
     constexpr int RPI = 1024 / RB;    // rows per copy instruction (64 lanes x 16 bytes)
     constexpr int RSW = 256 / RB;     // rows per 256-byte line of the 64 LDS banks
-    constexpr int TM = BM / 64, TN = BN / 64;
-    constexpr int AI = BM / (4 * RPI), BI = BN / (4 * RPI);  // copy instructions per wave per step
+    constexpr int NW = WM * WN;        // waves
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+    constexpr int AI = BM / (NW * RPI), BI = BN / (NW * RPI);  // copy instructions per wave per step
+    static_assert(AI >= 1 && BI >= 1 && (BM / NW) % (RSW * CH) == 0 && (BN / NW) % (RSW * CH) == 0 &&
+                  (BM / WM) % (RSW * CH) == 0 && (BN / WN) % (RSW * CH) == 0,
+                  "wave row blocks must start on a swizzle period");
     constexpr int STAGE = (BM + BN) * RB;
     constexpr int KSTEPS = (E == E_FP8) ? RB / 64 : RB / 32;  // MFMAs along K per step
     static_assert(KSTEPS >= 2 && KSTEPS % 2 == 0, "fragment slots alternate within a step");
@@ -128,10 +135,10 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
     const uint32_t lrowi = lane / CH;
     const uint32_t lchunk0 = (lane % CH) ^ ((lrowi / RSW) % CH);
     const uint32_t lchunk1 = (lane % CH) ^ ((4u + lrowi / RSW) % CH);
-    const uint32_t va0 = (wave * (BM / 4) + lrowi) * ldab + lchunk0 * 16u;
-    const uint32_t va1 = (wave * (BM / 4) + lrowi) * ldab + lchunk1 * 16u;
-    const uint32_t vb0 = (wave * (BN / 4) + lrowi) * ldbb + lchunk0 * 16u;
-    const uint32_t vb1 = (wave * (BN / 4) + lrowi) * ldbb + lchunk1 * 16u;
+    const uint32_t va0 = (wave * (BM / NW) + lrowi) * ldab + lchunk0 * 16u;
+    const uint32_t va1 = (wave * (BM / NW) + lrowi) * ldab + lchunk1 * 16u;
+    const uint32_t vb0 = (wave * (BN / NW) + lrowi) * ldbb + lchunk0 * 16u;
+    const uint32_t vb1 = (wave * (BN / NW) + lrowi) * ldbb + lchunk1 * 16u;
 
     auto stage_ptr = [&](int64_t kt) __attribute__((always_inline)) -> uint8_t* {
         return lds + (uint32_t)(kt % NST) * STAGE;
@@ -150,25 +157,25 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
         uint32_t v = (j & 1) ? (va1 | chunk_oob(kt, lchunk1)) : (va0 | chunk_oob(kt, lchunk0));
         v |= kt < KT ? 0u : kOutOfRange;
         if constexpr (decltype(edge)::value)
-            v |= (int32_t)(wave * (BM / 4) + RPI * j + lrowi) < rows_a ? 0u : kOutOfRange;
-        load_lds_1k(ra, stage_ptr(kt) + wave * (BM / 4) * RB + j * 1024, v,
+            v |= (int32_t)(wave * (BM / NW) + RPI * j + lrowi) < rows_a ? 0u : kOutOfRange;
+        load_lds_1k(ra, stage_ptr(kt) + wave * (BM / NW) * RB + j * 1024, v,
                     (uint32_t)kt * RB + (uint32_t)(RPI * j) * ldab);
     };
     auto copy_b = [&](auto edge, int64_t kt, int j) __attribute__((always_inline)) {
         uint32_t v = (j & 1) ? (vb1 | chunk_oob(kt, lchunk1)) : (vb0 | chunk_oob(kt, lchunk0));
         v |= kt < KT ? 0u : kOutOfRange;
         if constexpr (decltype(edge)::value)
-            v |= (int32_t)(wave * (BN / 4) + RPI * j + lrowi) < rows_b ? 0u : kOutOfRange;
-        load_lds_1k(rb, stage_ptr(kt) + BM * RB + wave * (BN / 4) * RB + j * 1024, v,
+            v |= (int32_t)(wave * (BN / NW) + RPI * j + lrowi) < rows_b ? 0u : kOutOfRange;
+        load_lds_1k(rb, stage_ptr(kt) + BM * RB + wave * (BN / NW) * RB + j * 1024, v,
                     (uint32_t)kt * RB + (uint32_t)(RPI * j) * ldbb);
     };
 
     // ---- fragment reads: every fragment row of this lane has the same swz(row)
-    const uint32_t wm = wave >> 1, wn = wave & 1u;
+    const uint32_t wm = wave / WN, wn = wave % WN;
     const uint32_t lrow = lane & 31u, lgrp = lane >> 5;
     const uint32_t sw = (lrow / RSW) % CH;
-    const uint32_t a_row0 = (wm * (BM / 2) + lrow) * RB;
-    const uint32_t b_row0 = BM * RB + (wn * (BN / 2) + lrow) * RB;
+    const uint32_t a_row0 = (wm * (BM / WM) + lrow) * RB;
+    const uint32_t b_row0 = BM * RB + (wn * (BN / WN) + lrow) * RB;
 
     Frag fa[2][TM], fb[2][TN];
     auto read_frags = [&](const uint8_t* st, int s, int slot) __attribute__((always_inline)) {
@@ -288,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
     mfma_drain();
 
     // ---- epilogue
-    constexpr int WR = BM / 2, WC = BN / 2;  // this wave's sub-tile
+    constexpr int WR = BM / WM, WC = BN / WN;  // this wave's sub-tile
     const int64_t wrow0 = m0 + wm * WR, wcol0 = n0 + wn * WC;
     auto out_val = [&](int i, int j, int v) __attribute__((always_inline)) -> float {
         float x = acc[i][j][v];
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nt(TileArgs p)
         constexpr int OB = WC * 2;          // bytes per staged output row
         constexpr int NCH = OB / 16;        // 16-byte chunks per row
         constexpr int WBYTES = WR * OB;     // bytes per wave
-        static_assert(4 * WBYTES <= NST * STAGE, "epilogue staging must fit the stage buffers");
+        static_assert(NW * WBYTES <= NST * STAGE, "epilogue staging must fit the stage buffers");
         __syncthreads();  // every wave is done reading the stage buffers
         uint8_t* ep = lds + wave * WBYTES;
 #pragma unroll

@@ -6,19 +6,12 @@
 // skeleton of the same page (section 核心抽象与编程模型对比).
 //
 // Built on the NT kernel's machinery (tg_gemm_nt.hpp): A is copied straight
-// into an NA-deep LDS ring with an XOR swizzle and read into MFMA fragments,
-// with the same operand swap and staged fp16 epilogue.  B never passes
-// through a shared stage: each wave owns 32 columns of the tile, copies
-// their int4 words into its own LDS slot (alongside A's copies, NA steps
-// ahead), reads them back and dequantises each word with
-// tg::dequant_w4_word -- the routine tg_dequant_w4 also runs -- directly
-// into the MFMA operand registers, interleaved with the MFMAs.  Each weight
-// is dequantised once per workgroup.
-//
-// Copies retire in issue order, so a wait for one forces all older ones.  All
-// copies of step j+NA are issued right after the barrier of step j, and the
-// one wait per step (before that barrier, for step j+1) leaves the copies of
-// the NA-2 later steps in flight.
+// into an LDS ring with an XOR swizzle and read into MFMA fragments, with
+// the same operand swap and staged fp16 epilogue.  B never passes through a
+// shared stage: each wave copies its own columns' int4 words into LDS,
+// reads them back and dequantises each word with tg::dequant_w4_word -- the
+// routine tg_dequant_w4 also runs -- directly into the MFMA operand
+// registers, interleaved with the MFMAs.
 #pragma once
 
 #include "tg_gemm_nt.hpp"
@@ -52,9 +45,13 @@ constexpr int kW4MaxGroups = 128;  // K <= 16384
 // Requirements (checked by the host): K a multiple of 256 and at most
 // 128 * kW4MaxGroups, scales 4-byte aligned with an even row stride.
 //
-// Work split: the workgroup computes a BM x 128 tile; wave w owns columns
-// 32w .. 32w+31 and all BM rows (BM/32 accumulators of 32 x 32), so each
-// weight is dequantised by exactly one wave, straight into the MFMA operand.
+// Work split: the workgroup computes a BM x 128 tile with 8 waves, two per
+// SIMD.  Waves w and w+4 own columns 32(w%4) .. +31 and all BM rows; wave w
+// takes the even K steps and wave w+4 the odd ones, each into its own
+// accumulators (BM/32 blocks of 32 x 32), which are summed at the end.  The
+// two waves of a SIMD thus share its matrix unit and its VALU: one
+// dequantises while the other's MFMAs run.  Each weight is dequantised once,
+// by the one wave that multiplies it, straight into the MFMA operand.
 //
 // A K step is 128 wide (one scale group).  A 32x32x16 MFMA takes, in lane l,
 // eight k values of row/column l % 32; lanes 0..31 hold its k slots 0..7,
@@ -68,8 +65,16 @@ constexpr int kW4MaxGroups = 128;  // K <= 16384
 // per step; a column's 64 bytes of words per step are fetched by four
 // neighbouring lanes of one copy instruction (one request); the scales are
 // fetched once, before the K loop.
+//
+// Ring: NA steps of A and words in LDS, NA/2 per wave group.  The group
+// that runs a step also copies it (each of its 4 waves a quarter of A and
+// its own columns' words), NA-2 steps ahead: at the barrier that opens
+// group step k, the slot of the group's step k-2 is free and is refilled
+// with step k+NA-2.
+constexpr int kW4Threads = 512;
+
 template <int BM, int NA>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4(TileArgs p)
+__global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_w4(TileArgs p)
 {
     constexpr int BN = 128;
     constexpr int RB = 256;          // bytes of K per staged A row: 128 fp16
@@ -81,11 +86,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int AI = BM / 4 / RPI; // A copy instructions per wave per step
     constexpr int ASTAGE = BM * RB;
     constexpr int WSTAGE = 4 * 2048; // per step: 4 waves x 32 columns x 64 bytes of words
-    constexpr int CPS = AI + 2;      // copy instructions per wave per step
-    // at the barrier opening step j: the copies of step j+1 were issued in
-    // step j+1-NA, those of steps j+2 .. j+NA-1 may still fly
-    constexpr int WAIT_BAR = (NA - 2) * CPS;
-    static_assert(BM % 64 == 0 && NA >= 2 && (NA & (NA - 1)) == 0 && (NA - 1) * CPS <= 63,
+    constexpr int CPS = AI + 2;      // copy instructions per wave per group step
+    constexpr int PER = NA / 2;      // ring steps per group
+    // at the barrier opening group step k: the copies of step k were issued
+    // PER-1 group steps earlier; those of the PER-2 group steps after it may fly
+    constexpr int WAIT_BAR = (PER - 2) * CPS;
+    static_assert(BM % 64 == 0 && NA % 2 == 0 && PER >= 2 && (PER - 1) * CPS <= 63,
                   "tile / ring depth / copies in flight");
     typedef u32x4 Frag;
 
@@ -95,6 +101,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t grp = wave >> 2, wq = wave & 3u;  // K-step parity; column quarter
     const int64_t M = p.M, N = p.N, K = p.K;
     const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
     const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
@@ -110,80 +117,81 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const i32x4_t rq = make_rsrc((const uint8_t*)p.qw + n0 * p.ldq * 4);
     const i32x4_t rs = make_rsrc((const uint8_t*)p.scales + n0 * p.lds * 2);
 
-    // ---- A copies: wave w fills rows 16w .. 16w+15 of the stage, RPI rows
-    // per instruction; lane i lands at physical chunk i % 16 of its row r,
-    // which holds logical chunk (i % 16) ^ (r % 16)
+    // ---- A copies: wave quarter q fills rows 16q .. 16q+15 of the stage,
+    // RPI rows per instruction; lane i lands at physical chunk i % 16 of its
+    // row r, which holds logical chunk (i % 16) ^ (r % 16)
     uint32_t va[AI];
 #pragma unroll
     for (int j = 0; j < AI; ++j) {
-        const uint32_t r = wave * (BM / 4) + RPI * j + lane / CH;
+        const uint32_t r = wq * (BM / 4) + RPI * j + lane / CH;
         const uint32_t lc = (lane % CH) ^ (r % CH);
-        va[j] = (int32_t)r < rows_a ? (wave * (BM / 4) + lane / CH) * ldab + lc * 16u : kOutOfRange;
+        va[j] = (int32_t)r < rows_a ? (wq * (BM / 4) + lane / CH) * ldab + lc * 16u : kOutOfRange;
     }
-    // ---- word copies: instruction q of wave w, lane i fetches 16-byte chunk
-    // i % 4 of the 64 bytes of column 32w + 16q + i/4, landing at byte
-    // 64 * (16q + i/4) + 16 * (i % 4) of the wave's 2 KB
+    // ---- word copies: instruction q of wave quarter w, lane i fetches
+    // 16-byte chunk i % 4 of the 64 bytes of column 32w + 16q + i/4, landing
+    // at byte 64 * (16q + i/4) + 16 * (i % 4) of the quarter's 2 KB
     uint32_t vq[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const uint32_t c = wave * 32u + 16u * q + lane / 4u;
+        const uint32_t c = wq * 32u + 16u * q + lane / 4u;
         vq[q] = (int32_t)c < cols_b ? c * (uint32_t)(p.ldq * 4) + (lane % 4u) * 16u : kOutOfRange;
     }
-    auto copy_step = [&](uint32_t kt, uint32_t slot) __attribute__((always_inline)) {
+    auto copy_step = [&](uint32_t kt) __attribute__((always_inline)) {
+        const uint32_t slot = kt % NA;
         const uint32_t past = kt < KT ? 0u : kOutOfRange;  // past the last step: zeros, never used
 #pragma unroll
         for (int j = 0; j < AI; ++j)
-            load_lds_1k(ra, lds_a + slot * ASTAGE + (wave * (BM / 4) + RPI * j) * RB, va[j] | past,
+            load_lds_1k(ra, lds_a + slot * ASTAGE + (wq * (BM / 4) + RPI * j) * RB, va[j] | past,
                         kt * RB + (uint32_t)(RPI * j) * ldab);
 #pragma unroll
         for (int q = 0; q < 2; ++q)
-            load_lds_1k(rq, lds_w + slot * WSTAGE + wave * 2048 + q * 1024, vq[q] | past, kt * 64u);
+            load_lds_1k(rq, lds_w + slot * WSTAGE + wq * 2048 + q * 1024, vq[q] | past, kt * 64u);
     };
 
-    // ---- operands, read one whole step ahead into one of two register sets
+    // ---- operands of a step: A fragments one sub-step ahead (two register
+    // slots), this lane's 16 words and the step's scale
     const uint32_t lcol = lane & 31u, lhalf = lane >> 5;
     const uint32_t lsw = lcol % CH;
-    Frag fa[2][SUB][TM];
-    u32x4 words[2][2];
-    uint32_t scale[2];
-    auto read_a = [&](uint32_t slot, int set, int s) __attribute__((always_inline)) {
+    Frag fa[2][TM];
+    u32x4 words[2];
+    uint32_t scale;
+    auto read_a = [&](uint32_t slot, int s, int fs) __attribute__((always_inline)) {
         const uint8_t* sa = lds_a + slot * ASTAGE;
         const uint32_t cs = (((8u * lhalf + (uint32_t)s) ^ lsw) << 4);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-            fa[set][s][i] = lds128(sa, (i * 32 + lcol) * RB + cs);
+            fa[fs][i] = lds128(sa, (i * 32 + lcol) * RB + cs);
     };
-    auto read_b = [&](uint32_t kt, uint32_t slot, int set) __attribute__((always_inline)) {
-        const uint8_t* ws = lds_w + slot * WSTAGE + wave * 2048;
-        words[set][0] = lds128(ws, lcol * 64u + lhalf * 32u);
-        words[set][1] = lds128(ws, lcol * 64u + lhalf * 32u + 16u);
-        const uint32_t g = kt < KT ? kt : 0u;  // (the step after the last reads any valid entry)
-        scale[set] = *(const uint16_t*)(lds_s + ((wave * 32u + lcol) * G + g) * 2u);
+    auto read_b = [&](uint32_t kt, uint32_t slot) __attribute__((always_inline)) {
+        const uint8_t* ws = lds_w + slot * WSTAGE + wq * 2048;
+        words[0] = lds128(ws, lcol * 64u + lhalf * 32u);
+        words[1] = lds128(ws, lcol * 64u + lhalf * 32u + 16u);
+        scale = *(const uint16_t*)(lds_s + ((wq * 32u + lcol) * G + kt) * 2u);
     };
     const W4Consts wc = w4_consts(p.zero_point);
-    auto dequant = [&](int set, int s) __attribute__((always_inline)) {
-        const _Float16 sc = bit_cast<_Float16>((uint16_t)scale[set]);
-        return dequant_w4_word(words[set][s >> 2][s & 3], wc, f16x2{sc, sc});
+    auto dequant = [&](int s) __attribute__((always_inline)) {
+        const _Float16 sc = bit_cast<_Float16>((uint16_t)scale);
+        return dequant_w4_word(words[s >> 2][s & 3], wc, f16x2{sc, sc});
     };
 
     f32x16 acc[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
         acc[i] = f32x16{};
-    auto mma = [&](const Frag& b, int set, int s) __attribute__((always_inline)) {
+    auto mma = [&](const Frag& b, int fs) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-            acc[i] = Mfma32<E_F16>::run(b, fa[set][s][i], acc[i]);
+            acc[i] = Mfma32<E_F16>::run(b, fa[fs][i], acc[i]);
     };
 
     // ---- prologue: every scale of the tile's columns (column c's G scales
     // at lds_s + 2*G*c, fetched as G/2 four-byte pairs; instruction t of the
     // workgroup takes pairs 64t .. 64t+63 of the flattened column-major
-    // array; wave w issues t = w, w+4, ...), then the copies of steps
-    // 0 .. NA-1, then the operands of step 0
+    // array; wave w issues t = w, w+8, ...), then each group's copies of its
+    // first PER-1 steps
     {
         const uint32_t half = G / 2, pairs = BN * half;
-        for (uint32_t t = wave; t * 64u < pairs; t += 4u) {
+        for (uint32_t t = wave; t * 64u < pairs; t += 8u) {
             const uint32_t e = t * 64u + lane;
             const uint32_t c = e / half, d = e - c * half;
             const uint32_t v = (e < pairs && (int32_t)c < cols_b) ? c * (uint32_t)(p.lds * 2) + d * 4u : kOutOfRange;
@@ -191,40 +199,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         }
     }
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
-        copy_step((uint32_t)i, (uint32_t)i);
-    wait_copies<(NA - 1) * CPS>();  // scales and step 0 landed (this wave's part)
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < SUB; ++s)
-        read_a(0, 0, s);
-    read_b(0, 0, 0);
+    for (int u = 0; u < PER - 1; ++u)
+        copy_step(grp + 2u * u);
 
-    Frag b = dequant(0, 0);
-
-    // ---- one step, in a fixed order.  The barrier opens the step: every
-    // wave's copies of step kt+1 have landed, and every read of step kt's
-    // slot (issued during step kt-1) is done, so the slot is refilled right
-    // away.  The MFMAs then run on registers only.  Each sub-step interleaves
-    // its two MFMAs with the sixteen VALU instructions that dequantise the
-    // next word (the wave issues in order, so VALU work placed between two
-    // MFMAs runs while the first executes) and with the reads of step kt+1;
-    // the last sub-step dequantises word 0 of step kt+1.
-    auto step = [&](uint32_t kt, int cur) __attribute__((always_inline)) {
-        const uint32_t slot = kt % NA, next = (kt + 1) % NA;
-        const int nxt = cur ^ 1;
-        wait_copies<WAIT_BAR>();  // this wave's copies of step kt+1 landed
+    // ---- group steps.  The barrier opens each one (both groups pass it
+    // together): the group's copies of the step have landed for every wave,
+    // and every read of its previous step's slot is done, so that slot is
+    // refilled right away.  Each sub-step interleaves its two MFMAs with the
+    // VALU instructions that dequantise the next word and the A reads of the
+    // next sub-step.
+    for (uint32_t kt = grp; kt < KT; kt += 2) {
+        const uint32_t slot = kt % NA;
+        wait_copies<WAIT_BAR>();  // this wave's copies of step kt landed (and the scales)
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        copy_step(kt + NA, slot);
-        read_b(kt + 1, next, nxt);  // (stale, unused, after the last step)
+        copy_step(kt + NA - 2);  // into the slot of step kt-2
+        read_b(kt, slot);
+        read_a(slot, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        Frag b = dequant(0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
-            mma(b, cur, s);
-            read_a(next, nxt, s);
-            b = s + 1 < SUB ? dequant(cur, s + 1) : dequant(nxt, 0);
-            // MFMA, 8 VALU, 1 LDS read, MFMA, 8 VALU, 1 LDS read
+            mma(b, s & 1);
+            if (s + 1 < SUB) {
+                read_a(slot, s + 1, (s + 1) & 1);
+                b = dequant(s + 1);
+            }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -233,31 +234,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    for (uint32_t kt = 0; kt < KT; kt += 2) {  // KT is even
-        step(kt, 0);
-        step(kt + 1, 1);
-#pragma unroll
-        for (int s = 0; s < SUB; ++s)
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                pin(fa[0][s][i]);
-        pin(words[0][0]);
-        pin(words[0][1]);
-        pin(scale[0]);
-        pin(b);
     }
     wait_copies<0>();  // every copy (including those past the last step) has landed
     mfma_drain();
 
-    // ---- epilogue (fp16): each wave stages its BM x 32 sub-tile in LDS and
-    // stores 16-byte row pieces.  Accumulator value v of lane l holds row
-    // 32i + l%32, column 8*(v/4) + 4*(l/32) + v%4 of the wave's columns.
-    constexpr int WR = BM, OB = 64, NCH = 4, WBYTES = WR * OB;
-    static_assert(4 * WBYTES <= NA * ASTAGE, "epilogue staging must fit the A ring");
-    const int64_t wrow0 = m0, wcol0 = n0 + wave * 32;
+    // ---- sum the two groups' accumulators: group 1 leaves its blocks in
+    // LDS (lane-contiguous 16-byte pieces), group 0 adds them
+    constexpr int PBYTES = 4 * TM * 16 * 64 * 4;  // 4 waves x TM blocks x 16 floats x 64 lanes
     __syncthreads();
-    uint8_t* ep = lds_a + wave * WBYTES;
+    uint8_t* part = lds_a + wq * (PBYTES / 4);
+    if (grp == 1) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4)
+                sts128(part, ((i * 4 + v4) * 64 + lane) * 16u,
+                       bit_cast<u32x4>(f32x4{acc[i][4 * v4], acc[i][4 * v4 + 1], acc[i][4 * v4 + 2], acc[i][4 * v4 + 3]}));
+    }
+    __syncthreads();
+    if (grp == 1)
+        return;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const f32x4 o = bit_cast<f32x4>(lds128(part, ((i * 4 + v4) * 64 + lane) * 16u));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[i][4 * v4 + e] += o[e];
+        }
+
+    // ---- epilogue (fp16, group 0): each wave stages its BM x 32 sub-tile in
+    // LDS and stores 16-byte row pieces.  Accumulator value v of lane l holds
+    // row 32i + l%32, column 8*(v/4) + 4*(l/32) + v%4 of the wave's columns.
+    constexpr int WR = BM, OB = 64, NCH = 4, WBYTES = WR * OB;
+    static_assert(PBYTES + 4 * WBYTES <= NA * ASTAGE, "partials and staging must fit the A ring");
+    const int64_t wrow0 = m0, wcol0 = n0 + wq * 32;
+    uint8_t* ep = lds_a + PBYTES + wq * WBYTES;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const uint32_t r = i * 32 + lcol;

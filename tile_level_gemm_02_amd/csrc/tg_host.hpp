@@ -108,6 +108,11 @@ inline bool nt_eligible(const TileArgs& a)
 // Staging depth of the NT kernel: bytes of K per staged row and number of stages.
 template <int E> struct NtStaging { static constexpr int RB = 128, NST = 2; };
 
+// Waves of the NT kernel per tile: the 256 x 256 tile takes 8 (2 x 4, two
+// per SIMD) for the LDS read rate its fragments need; smaller tiles take 4.
+template <int BM, int BN> struct NtWaves { static constexpr int WM = 2, WN = 2; };
+template <> struct NtWaves<256, 256> { static constexpr int WM = 2, WN = 4; };
+
 template <int E, int O, int BM, int BN>
 tg_status launch_nt(const TileArgs& a, hipStream_t s)
 {
@@ -115,7 +120,8 @@ tg_status launch_nt(const TileArgs& a, hipStream_t s)
     if (tiles > 0x7FFFFFFF)
         return TG_ERR_NOT_SUPPORTED;
     constexpr int RB = NtStaging<E>::RB, NST = NtStaging<E>::NST;
-    hipLaunchKernelGGL((gemm_nt<E, O, BM, BN, RB, NST>), dim3((uint32_t)tiles), dim3(kThreads), 0, s, a);
+    constexpr int WM = NtWaves<BM, BN>::WM, WN = NtWaves<BM, BN>::WN;
+    hipLaunchKernelGGL((gemm_nt<E, O, BM, BN, RB, NST, WM, WN>), dim3((uint32_t)tiles), dim3(64 * WM * WN), 0, s, a);
     return launched();
 }
 

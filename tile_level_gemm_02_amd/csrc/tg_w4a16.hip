@@ -102,7 +102,7 @@ extern "C" tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* 
         const int64_t tiles = tg::n_tiles<BM, BN>(M, N);
         if (tiles > 0x7FFFFFFF)
             return TG_ERR_NOT_SUPPORTED;
-        hipLaunchKernelGGL((tg::gemm_w4<BM, NA>), dim3((uint32_t)tiles), dim3(tg::kThreads), 0, s, a);
+        hipLaunchKernelGGL((tg::gemm_w4<BM, NA>), dim3((uint32_t)tiles), dim3(tg::kW4Threads), 0, s, a);
         return tg::launched();
     }
     if (tg::n_tiles<128, 128>(M, N) >= 96)
