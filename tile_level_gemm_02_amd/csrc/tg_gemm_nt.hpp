@@ -6,18 +6,20 @@
 // Dataflow of the single-GPU GEMM skeleton in "TileScale 与 TileLang比较"
 // (section 核心抽象与编程模型对比), mapped onto CDNA4:
 //
-//  * grid of output tiles: one 256-thread workgroup (4 waves, 2 x 2) per
-//    BM x BN tile, ordered XCD-aware (tile_coords);
+//  * grid of output tiles: one workgroup of WM x WN waves per BM x BN tile,
+//    ordered XCD-aware (tile_coords);
 //  * global -> shared copy: buffer loads that write LDS directly (no
 //    registers, no ds_write), 16 bytes per lane, 8 rows of 128 bytes per wave
 //    instruction, into XOR-swizzled rows; tails need no branches: rows past
-//    M or N are clamped to the last valid row (they only feed outputs that are
-//    never stored), 16-byte chunks past K read through an out-of-range offset,
-//    which the buffer unit returns as zeros;
-//  * pipelined K loop: NST LDS stages of RB bytes of K per row; the copies of
-//    step k+NST-1 and k+NST are issued between the MFMAs of step k (spread, so
-//    the in-order issue never blocks on a full address FIFO), each with NST-1
-//    steps to land before the barrier that publishes it;
+//    M or N and 16-byte chunks past K read through an out-of-range offset,
+//    which the buffer unit returns as zeros (such rows only feed outputs that
+//    are never stored);
+//  * pipelined K loop: a ring of NH LDS half-stages (one holds the A rows or
+//    the B rows of one K step: RB bytes of K per row); half-stage h is A of
+//    step h/2 for even h and B of step h/2 for odd h.  Each K step frees two
+//    half-stages and refills them (copies spread between the MFMAs, so the
+//    in-order issue never blocks on a full address FIFO).  NH = 4 is two
+//    full stages; NH = 5 gives the A rows most of a further step to land;
 //  * tile GEMM into register fragments: LDS -> VGPR fragments double-buffered
 //    across the K sub-steps (the reads of sub-step s+1 are in flight while
 //    the MFMAs of sub-step s run), 32x32 MFMAs accumulating in fp32 AGPRs;
@@ -80,7 +82,7 @@ __device__ __forceinline__ void wait_copies()
 // WM x WN waves share the tile (each computes a BM/WM x BN/WN sub-tile).
 // With 8 waves (two per SIMD) the LDS sustains about twice the fragment-read
 // rate of 4 waves (one per SIMD), which the 256 x 256 tile needs.
-template <int E, int O, int BM, int BN, int RB, int NST, int WM = 2, int WN = 2>
+template <int E, int O, int BM, int BN, int RB, int NH, int WM = 2, int WN = 2>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
 {
     constexpr int EB = ElemInfo<E>::bytes;
@@ -95,13 +97,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     static_assert(AI >= 1 && BI >= 1 && (BM / NW) % (RSW * CH) == 0 && (BN / NW) % (RSW * CH) == 0 &&
                   (BM / WM) % (RSW * CH) == 0 && (BN / WN) % (RSW * CH) == 0,
                   "wave row blocks must start on a swizzle period");
-    constexpr int STAGE = (BM + BN) * RB;
+    constexpr int HALF = BM * RB;     // bytes of one half-stage (A and B tiles are square)
     constexpr int KSTEPS = (E == E_FP8) ? RB / 64 : RB / 32;  // MFMAs along K per step
     static_assert(KSTEPS >= 2 && KSTEPS % 2 == 0, "fragment slots alternate within a step");
-    static_assert(NST >= 2 && (NST - 2) * (AI + BI) + AI <= 63, "copies in flight");
+    static_assert(BM == BN && AI == BI, "square tiles: A and B half-stages alike");
+    static_assert(NH >= 4 && (NH - 3) * AI <= 63, "copies in flight");
     typedef typename Mfma32<E>::frag Frag;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NH * HALF];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases scalar
@@ -140,8 +143,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     const uint32_t vb0 = (wave * (BN / NW) + lrowi) * ldbb + lchunk0 * 16u;
     const uint32_t vb1 = (wave * (BN / NW) + lrowi) * ldbb + lchunk1 * 16u;
 
-    auto stage_ptr = [&](int64_t kt) __attribute__((always_inline)) -> uint8_t* {
-        return lds + (uint32_t)(kt % NST) * STAGE;
+    // half-stage of A (or B) of K step kt
+    auto a_ptr = [&](int64_t kt) __attribute__((always_inline)) -> uint8_t* {
+        return lds + (uint32_t)((2 * kt) % NH) * HALF;
+    };
+    auto b_ptr = [&](int64_t kt) __attribute__((always_inline)) -> uint8_t* {
+        return lds + (uint32_t)((2 * kt + 1) % NH) * HALF;
     };
     auto chunk_oob = [&](int64_t kt, uint32_t lchunk) __attribute__((always_inline)) -> uint32_t {
         // a chunk at or past K (only in the last step) reads through an
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         v |= kt < KT ? 0u : kOutOfRange;
         if constexpr (decltype(edge)::value)
             v |= (int32_t)(wave * (BM / NW) + RPI * j + lrowi) < rows_a ? 0u : kOutOfRange;
-        load_lds_1k(ra, stage_ptr(kt) + wave * (BM / NW) * RB + j * 1024, v,
+        load_lds_1k(ra, a_ptr(kt) + wave * (BM / NW) * RB + j * 1024, v,
                     (uint32_t)kt * RB + (uint32_t)(RPI * j) * ldab);
     };
     auto copy_b = [&](auto edge, int64_t kt, int j) __attribute__((always_inline)) {
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         v |= kt < KT ? 0u : kOutOfRange;
         if constexpr (decltype(edge)::value)
             v |= (int32_t)(wave * (BN / NW) + RPI * j + lrowi) < rows_b ? 0u : kOutOfRange;
-        load_lds_1k(rb, stage_ptr(kt) + BM * RB + wave * (BN / NW) * RB + j * 1024, v,
+        load_lds_1k(rb, b_ptr(kt) + wave * (BN / NW) * RB + j * 1024, v,
                     (uint32_t)kt * RB + (uint32_t)(RPI * j) * ldbb);
     };
 
@@ -175,10 +182,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     const uint32_t lrow = lane & 31u, lgrp = lane >> 5;
     const uint32_t sw = (lrow / RSW) % CH;
     const uint32_t a_row0 = (wm * (BM / WM) + lrow) * RB;
-    const uint32_t b_row0 = BM * RB + (wn * (BN / WN) + lrow) * RB;
+    const uint32_t b_row0 = (wn * (BN / WN) + lrow) * RB;
 
     Frag fa[2][TM], fb[2][TN];
-    auto read_frags = [&](const uint8_t* st, int s, int slot) __attribute__((always_inline)) {
+    auto read_frags = [&](int64_t kt, int s, int slot) __attribute__((always_inline)) {
+        const uint8_t* st = a_ptr(kt);
+        const uint8_t* sb = b_ptr(kt);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             if constexpr (E == E_FP8) {
@@ -195,12 +204,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         for (int j = 0; j < TN; ++j) {
             if constexpr (E == E_FP8) {
                 const uint32_t c0 = (uint32_t)(4 * s) + 2u * lgrp;
-                const u32x4 lo = lds128(st, b_row0 + j * 32 * RB + ((c0 ^ sw) << 4));
-                const u32x4 hi = lds128(st, b_row0 + j * 32 * RB + (((c0 + 1u) ^ sw) << 4));
+                const u32x4 lo = lds128(sb, b_row0 + j * 32 * RB + ((c0 ^ sw) << 4));
+                const u32x4 hi = lds128(sb, b_row0 + j * 32 * RB + (((c0 + 1u) ^ sw) << 4));
                 fb[slot][j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
             } else {
-                fb[slot][j] = lds128(st, b_row0 + j * 32 * RB + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
+                fb[slot][j] = lds128(sb, b_row0 + j * 32 * RB + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
             }
         }
     };
@@ -238,50 +247,50 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     };
     auto nothing = [](int) {};
 
-    // One K step out of stage kt % NST.  Entering, the fragments of its
-    // sub-step 0 are in slot 0.  The B copies of step kt+NST-1 go out between
-    // the sub-step-0 MFMAs (their stage was freed by the previous barrier).
-    // The barrier before the last sub-step publishes step kt+1 (copies of
-    // steps past kt+1 may still be in flight) and frees stage kt % NST: the A
-    // copies of step kt+NST go out between the last sub-step's MFMAs, while
-    // the first fragments of step kt+1 are read.
+    // copy instruction q of half-stage h (A of step h/2 for even h, B for odd h)
+    auto copy_half = [&](auto edge, int64_t h, int q) __attribute__((always_inline)) {
+        if ((h & 1) == 0)
+            copy_a(edge, h >> 1, q);
+        else
+            copy_b(edge, h >> 1, q);
+    };
+
+    // One K step.  Entering, the fragments of its sub-step 0 are in slot 0.
+    // Half-stage 2kt+NH-1 (whose slot was freed by the previous barrier) is
+    // copied between the sub-step-0 MFMAs.  The barrier before the last
+    // sub-step publishes step kt+1 (half-stages past 2kt+3 may still be in
+    // flight) and frees the two half-stages of step kt: half-stage 2kt+NH is
+    // copied between the last sub-step's MFMAs, while the first fragments of
+    // step kt+1 are read.
     auto step = [&](auto edge, int64_t kt) __attribute__((always_inline)) {
-        const uint8_t* cur = stage_ptr(kt);
 #pragma unroll
         for (int s = 0; s < KSTEPS - 1; ++s) {
-            read_frags(cur, s + 1, (s + 1) & 1);
+            read_frags(kt, s + 1, (s + 1) & 1);
             if (s == 0)
-                mma(s & 1, [&](int q) __attribute__((always_inline)) { copy_b(edge, kt + NST - 1, q); },
-                    std::integral_constant<int, BI>{});
+                mma(s & 1, [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH - 1, q); },
+                    std::integral_constant<int, AI>{});
             else
                 mma(s & 1, nothing, std::integral_constant<int, 0>{});
         }
         __builtin_amdgcn_sched_barrier(0);
-        wait_copies<(NST - 2) * (AI + BI)>();  // own copies of step kt+1 landed ...
-        __syncthreads();                        // ... and every wave's; stage kt % NST is free
+        wait_copies<(NH - 4) * AI>();  // own copies of step kt+1 landed ...
+        __syncthreads();               // ... and every wave's; the half-stages of step kt are free
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(stage_ptr(kt + 1), 0, 0);   // (stale, unused, after the last step)
-        mma((KSTEPS - 1) & 1, [&](int q) __attribute__((always_inline)) { copy_a(edge, kt + NST, q); },
+        read_frags(kt + 1, 0, 0);      // (stale, unused, after the last step)
+        mma((KSTEPS - 1) & 1, [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH, q); },
             std::integral_constant<int, AI>{});
     };
 
     auto run = [&](auto edge) __attribute__((always_inline)) {
-        // steps 0 .. NST-2 complete, plus the A half of step NST-1
+        // half-stages 0 .. NH-2
 #pragma unroll
-        for (int st = 0; st < NST - 1; ++st) {
+        for (int h = 0; h < NH - 1; ++h)
 #pragma unroll
             for (int j = 0; j < AI; ++j)
-                copy_a(edge, st, j);
-#pragma unroll
-            for (int j = 0; j < BI; ++j)
-                copy_b(edge, st, j);
-        }
-#pragma unroll
-        for (int j = 0; j < AI; ++j)
-            copy_a(edge, NST - 1, j);
-        wait_copies<(NST - 2) * (AI + BI) + AI>();  // step 0 landed
+                copy_half(edge, h, j);
+        wait_copies<(NH - 3) * AI>();  // step 0 landed
         __syncthreads();
-        read_frags(stage_ptr(0), 0, 0);
+        read_frags(0, 0, 0);
         for (int64_t kt = 0; kt < KT; ++kt)
             step(edge, kt);
         wait_copies<0>();  // copies past the last step (zeros) must land before LDS is reused
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         constexpr int OB = WC * 2;          // bytes per staged output row
         constexpr int NCH = OB / 16;        // 16-byte chunks per row
         constexpr int WBYTES = WR * OB;     // bytes per wave
-        static_assert(NW * WBYTES <= NST * STAGE, "epilogue staging must fit the stage buffers");
+        static_assert(NW * WBYTES <= NH * HALF, "epilogue staging must fit the stage buffers");
         __syncthreads();  // every wave is done reading the stage buffers
         uint8_t* ep = lds + wave * WBYTES;
 #pragma unroll

@@ -105,8 +105,11 @@ inline bool nt_eligible(const TileArgs& a)
     return (a.K % (16 / EB)) == 0 && 256 * a.lda * EB + a.K * EB < lim && 256 * a.ldb * EB + a.K * EB < lim;
 }
 
-// Staging depth of the NT kernel: bytes of K per staged row and number of stages.
-template <int E> struct NtStaging { static constexpr int RB = 128, NST = 2; };
+// Staging of the NT kernel: bytes of K per staged row, and LDS half-stages in
+// the ring.  Four (two full stages) measured faster than five on the 256 x 256
+// tile at 4096^3 (the fifth fills the LDS: 5 x 32 KB).
+template <int E> struct NtStaging { static constexpr int RB = 128; };
+template <int BM> struct NtRing { static constexpr int NH = 4; };
 
 // Waves of the NT kernel per tile: the 256 x 256 tile takes 8 (2 x 4, two
 // per SIMD) for the LDS read rate its fragments need; smaller tiles take 4.
@@ -119,9 +122,9 @@ tg_status launch_nt(const TileArgs& a, hipStream_t s)
     const int64_t tiles = n_tiles<BM, BN>(a.M, a.N);
     if (tiles > 0x7FFFFFFF)
         return TG_ERR_NOT_SUPPORTED;
-    constexpr int RB = NtStaging<E>::RB, NST = NtStaging<E>::NST;
+    constexpr int RB = NtStaging<E>::RB, NH = NtRing<BM>::NH;
     constexpr int WM = NtWaves<BM, BN>::WM, WN = NtWaves<BM, BN>::WN;
-    hipLaunchKernelGGL((gemm_nt<E, O, BM, BN, RB, NST, WM, WN>), dim3((uint32_t)tiles), dim3(64 * WM * WN), 0, s, a);
+    hipLaunchKernelGGL((gemm_nt<E, O, BM, BN, RB, NH, WM, WN>), dim3((uint32_t)tiles), dim3(64 * WM * WN), 0, s, a);
     return launched();
 }
 
