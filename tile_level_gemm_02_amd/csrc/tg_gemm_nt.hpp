@@ -185,33 +185,32 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     const uint32_t b_row0 = (wn * (BN / WN) + lrow) * RB;
 
     Frag fa[2][TM], fb[2][TN];
+    // fragment read r (0 .. TM+TN-1) of sub-step s of K step kt into slot
+    // `slot`, numbered in the order the MFMAs consume them: A row block 0,
+    // every B column block, then A row blocks 1 .. TM-1
+    auto read_frag = [&](int64_t kt, int s, int slot, int r) __attribute__((always_inline)) {
+        const bool is_a = (r == 0) || (r > TN);
+        const int idx = (r == 0) ? 0 : (r <= TN ? r - 1 : r - TN);
+        const uint8_t* st = is_a ? a_ptr(kt) : b_ptr(kt);
+        const uint32_t row0 = (is_a ? a_row0 : b_row0) + (uint32_t)idx * 32 * RB;
+        Frag f;
+        if constexpr (E == E_FP8) {
+            const uint32_t c0 = (uint32_t)(4 * s) + 2u * lgrp;
+            const u32x4 lo = lds128(st, row0 + ((c0 ^ sw) << 4));
+            const u32x4 hi = lds128(st, row0 + (((c0 + 1u) ^ sw) << 4));
+            f = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        } else {
+            f = lds128(st, row0 + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
+        }
+        if (is_a)
+            fa[slot][idx] = f;
+        else
+            fb[slot][idx] = f;
+    };
     auto read_frags = [&](int64_t kt, int s, int slot) __attribute__((always_inline)) {
-        const uint8_t* st = a_ptr(kt);
-        const uint8_t* sb = b_ptr(kt);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            if constexpr (E == E_FP8) {
-                const uint32_t c0 = (uint32_t)(4 * s) + 2u * lgrp;
-                const u32x4 lo = lds128(st, a_row0 + i * 32 * RB + ((c0 ^ sw) << 4));
-                const u32x4 hi = lds128(st, a_row0 + i * 32 * RB + (((c0 + 1u) ^ sw) << 4));
-                fa[slot][i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            } else {
-                fa[slot][i] = lds128(st, a_row0 + i * 32 * RB + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            if constexpr (E == E_FP8) {
-                const uint32_t c0 = (uint32_t)(4 * s) + 2u * lgrp;
-                const u32x4 lo = lds128(sb, b_row0 + j * 32 * RB + ((c0 ^ sw) << 4));
-                const u32x4 hi = lds128(sb, b_row0 + j * 32 * RB + (((c0 + 1u) ^ sw) << 4));
-                fb[slot][j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            } else {
-                fb[slot][j] = lds128(sb, b_row0 + j * 32 * RB + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
-            }
-        }
+        for (int r = 0; r < TM + TN; ++r)
+            read_frag(kt, s, slot, r);
     };
 
     f32x16 acc[TM][TN];
@@ -224,25 +223,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     // acc[i][j] holds the transposed 32x32 block (B rows x A rows): value v of
     // lane l is C[m = i*32 + l%32][n = j*32 + 8*(v/4) + 4*(l/32) + v%4], so every
     // lane owns runs of 4 consecutive output columns.
-    // The TM*TN MFMAs of one sub-step; the calls `between(q)` (q = 0 .. NQ-1)
-    // are spread evenly over them and pinned in place, so copies interleave
-    // with the matrix instructions instead of stalling the wave's in-order
-    // issue in one burst.
-    auto mma = [&](int slot, auto between, auto nq) __attribute__((always_inline)) {
+    //
+    // One sub-step: the TM*TN MFMAs of fragment slot `slot`.  The fragment
+    // reads of the next sub-step and the NQ copy instructions are spread
+    // evenly over the MFMAs (copies from the first MFMA on, so they get the
+    // most time to land), each pinned in place: the wave's in-order issue
+    // never waits on a burst of LDS reads or on a full address queue.
+    constexpr int NT = TM * TN, NR = TM + TN;
+    auto substep = [&](int slot, auto rd, auto cp, auto nq) __attribute__((always_inline)) {
         constexpr int NQ = decltype(nq)::value;
 #pragma unroll
-        for (int t = 0; t < TM * TN; ++t) {
+        for (int t = 0; t < NT; ++t) {
             const int i = t / TN, j = t % TN;
             acc[i][j] = Mfma32<E>::run(fb[slot][j], fa[slot][i], acc[i][j]);
-            if constexpr (NQ > 0) {
-                const int q0 = t * NQ / (TM * TN), q1 = (t + 1) * NQ / (TM * TN);
-                if (q1 > q0) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    for (int q = q0; q < q1; ++q)
-                        between(q);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                if (r * NT / NR == t)
+                    rd(r);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                if (q * NT / NQ == t)
+                    cp(q);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     auto nothing = [](int) {};
@@ -257,28 +260,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
 
     // One K step.  Entering, the fragments of its sub-step 0 are in slot 0.
     // Half-stage 2kt+NH-1 (whose slot was freed by the previous barrier) is
-    // copied between the sub-step-0 MFMAs.  The barrier before the last
-    // sub-step publishes step kt+1 (half-stages past 2kt+3 may still be in
-    // flight) and frees the two half-stages of step kt: half-stage 2kt+NH is
-    // copied between the last sub-step's MFMAs, while the first fragments of
-    // step kt+1 are read.
+    // copied during sub-step 0.  The barrier before the last sub-step
+    // publishes step kt+1 (half-stages past 2kt+3 may still be in flight) and
+    // frees the two half-stages of step kt: half-stage 2kt+NH is copied during
+    // the last sub-step, while the first fragments of step kt+1 are read.
     auto step = [&](auto edge, int64_t kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < KSTEPS - 1; ++s) {
-            read_frags(kt, s + 1, (s + 1) & 1);
+            auto rd = [&](int r) __attribute__((always_inline)) { read_frag(kt, s + 1, (s + 1) & 1, r); };
             if (s == 0)
-                mma(s & 1, [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH - 1, q); },
-                    std::integral_constant<int, AI>{});
+                substep(s & 1, rd, [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH - 1, q); },
+                        std::integral_constant<int, AI>{});
             else
-                mma(s & 1, nothing, std::integral_constant<int, 0>{});
+                substep(s & 1, rd, nothing, std::integral_constant<int, 0>{});
         }
         __builtin_amdgcn_sched_barrier(0);
         wait_copies<(NH - 4) * AI>();  // own copies of step kt+1 landed ...
         __syncthreads();               // ... and every wave's; the half-stages of step kt are free
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(kt + 1, 0, 0);      // (stale, unused, after the last step)
-        mma((KSTEPS - 1) & 1, [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH, q); },
-            std::integral_constant<int, AI>{});
+        // (the reads of step kt+1 after the last step are stale and unused)
+        substep((KSTEPS - 1) & 1, [&](int r) __attribute__((always_inline)) { read_frag(kt + 1, 0, 0, r); },
+                [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH, q); },
+                std::integral_constant<int, AI>{});
     };
 
     auto run = [&](auto edge) __attribute__((always_inline)) {
