@@ -13,7 +13,8 @@ Printed: ONE JSON line with the metric, `roofline` (the GEMM kernel's
 achieved TFLOP/s against the dense bf16 MFMA peak, from HIP events around
 each launch inside the timed region), `cpu_baseline` (the CPU oracle timed
 on a bounded sample of the same workload) and `secondary` (the skinny M=16
-GEMM's GB/s against the HBM peak, the fp8 and w4a16 workloads), each
+GEMM's GB/s against the HBM peak, the fp8 and w4a16 workloads, and the
+w4a16 weights at decode batch sizes M=16 and M=1), each
 secondary timed launch by launch with the 256 MB Infinity Cache flushed
 (by a 512 MiB read) before every launch.
 """
@@ -141,12 +142,12 @@ def setup_fp8():
     return w, fn, flops, bytes_
 
 
-def setup_w4a16():
+def setup_w4a16(M=None):
     import torch
     import synth
     import tile_level_gemm_02_amd as tg
 
-    w = synth.workload("w4a16")
+    w = synth.workload("w4a16", M=M)
     A, q, s = w["A"].cuda(), w["qweight"].cuda(), w["scales"].cuda()
     C = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
     fn = lambda: tg.tg_gemm_w4a16(A, q, s, C)
@@ -195,7 +196,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (to scale HBM byte counters)")
-    ap.add_argument("--only", choices=["bf16_4096", "bf16_skinny", "fp8_8192", "w4a16"], default=None,
+    ap.add_argument("--only", choices=["bf16_4096", "bf16_skinny", "fp8_8192", "w4a16", "w4a16_m16", "w4a16_m1"],
+                    default=None,
                     help="only run this workload's launches (for counter collection), no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -223,7 +225,8 @@ def main():
     flush = make_flush()
     if args.only:
         setup = {"bf16_4096": setup_bf16_4096, "bf16_skinny": setup_skinny, "fp8_8192": setup_fp8,
-                 "w4a16": setup_w4a16}[args.only]
+                 "w4a16": setup_w4a16, "w4a16_m16": lambda: setup_w4a16(16),
+                 "w4a16_m1": lambda: setup_w4a16(1)}[args.only]
         _, fn, _, _ = setup()
         for _ in range(args.warmup):
             fn()
@@ -281,7 +284,9 @@ def main():
         sec = {}
         n = max(10, min(args.steps, 50))
         for name, setup, peak_key in (("bf16_skinny", setup_skinny, "hbm"), ("fp8_8192", setup_fp8, "fp8"),
-                                      ("w4a16", setup_w4a16, "both")):
+                                      ("w4a16", setup_w4a16, "both"),
+                                      ("w4a16_m16", lambda: setup_w4a16(16), "hbm"),
+                                      ("w4a16_m1", lambda: setup_w4a16(1), "hbm")):
             w2, fn2, fl2, by2 = setup()
             for _ in range(3):
                 fn2()

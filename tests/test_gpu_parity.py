@@ -254,6 +254,47 @@ def test_w4a16_layouts(tg, case):
     assert ok, (case, r, idx)
 
 
+# M <= 16: the decode kernel (eight waves split the 128-K groups; a group
+# count below, equal to and not a multiple of the wave count, batches of two
+# groups plus a tail), ragged N, every zero point at the ends of its range
+@pytest.mark.parametrize("shape", [(1, 8, 128), (2, 40, 384), (7, 100, 1152), (16, 33, 256),
+                                   (16, 520, 2176), (5, 64, 1024), (1, 1000, 4096)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("zp", [0, 15])
+def test_w4a16_decode(tg, shape, zp):
+    M, N, K = shape
+    A, q, s = _w4_inputs(M, N, K, seed=7 * M + N + zp)
+    C = _run_w4(tg, A, q, s, zp=zp)
+    cref, S = oracle.w4a16(A, q, s, K, zero_point=zp)
+    ok, r, idx = ochk.check(_f64(C), cref, S, K, "f16")
+    assert ok, (r, idx)
+
+
+# the decode kernel with row strides above the minimum on every operand
+# (odd scale stride, scales only 2-byte aligned) and K == 0 (zeros stored)
+def test_w4a16_decode_layouts_and_k0(tg):
+    M, N, K = 11, 72, 640
+    A, q, s = _w4_inputs(M, N, K, seed=43)
+    big = torch.zeros(N * (K // 128 + 2) + 1, dtype=torch.float16, device="cuda")
+    sd = big[1:].view(N, K // 128 + 2)[:, : K // 128]
+    sd.copy_(s.cuda())
+    assert sd.data_ptr() % 4 == 2 and sd.stride(0) % 2 == 1
+    Cbuf = torch.full((M, N + 16), float("nan"), dtype=torch.float16, device="cuda")
+    C = Cbuf[:, :N]
+    tg.tg_gemm_w4a16(_gpu_strided(A, 40), _gpu_strided(q, 8), sd, C)
+    torch.cuda.synchronize()
+    cref, S = oracle.w4a16(A, q, s, K)
+    ok, r, idx = ochk.check(_f64(C), cref, S, K, "f16")
+    assert ok, (r, idx)
+    assert torch.isnan(Cbuf[:, N:]).all()
+    A0 = torch.zeros((M, 0), dtype=torch.float16, device="cuda")
+    q0 = torch.zeros((N, 0), dtype=torch.int32, device="cuda")
+    s0 = torch.zeros((N, 0), dtype=torch.float16, device="cuda")
+    tg.tg_gemm_w4a16(A0, q0, s0, C)
+    torch.cuda.synchronize()
+    assert torch.all(C == 0) and torch.isnan(Cbuf[:, N:]).all()
+
+
 @pytest.mark.parametrize("zp", [0, 8, 15])
 def test_dequant_bit_exact(tg, zp):
     N, K = 300, 1024
@@ -347,3 +388,14 @@ def test_workload_w4a16(tg):
     tg.tg_dequant_w4(q.cuda(), s.cuda(), W, K)
     torch.cuda.synchronize()
     assert np.array_equal(W.cpu().view(torch.int16).numpy().view(np.uint16), oracle.dequant_w4(q, s, K))
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_workload_w4a16_decode(tg, M):
+    """The w4a16 workload's weights at decode batch sizes, every output checked."""
+    w = synth.workload("w4a16", M=M)
+    A, q, s, K = w["A"], w["qweight"], w["scales"], w["K"]
+    C = _run_w4(tg, A, q, s)
+    cref, S = oracle.w4a16(A, q, s, K)
+    ok, r, idx = ochk.check(_f64(C), cref, S, K, "f16")
+    assert ok, (r, idx)

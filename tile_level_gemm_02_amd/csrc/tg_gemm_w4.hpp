@@ -304,4 +304,135 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2
     }
 }
 
+// --------------------------------------------------------------------------
+// w4a16 for M <= 16 rows (decode).  Streaming the int4 weights from HBM is
+// the whole cost, so nothing is staged in LDS: each lane loads 16 bytes of
+// its column's words per 128-K group -- four words, 32 consecutive k -- and
+// dequantises each word with tg::dequant_w4_word straight into the B operand
+// of a 16x16x32 MFMA (M padded to 16 rows, rows past M read as zeros).
+//
+// K order inside an MFMA: the four lane quarters h = 0..3 of a 16x16x32 MFMA
+// each supply 8 k values.  MFMA j (0..3) of a group gives quarter h the k
+// = 128g + 32h + 8j .. +7, i.e. word 4h + j of the group: each lane's four
+// words are one aligned 16-byte chunk, and its A operands are the four
+// 16-byte chunks of the same 32 k of its row.  A and B agree on every k, so
+// the sum is the group's full dot product.
+//
+// The waves of a workgroup split the K groups and reduce their partial tiles
+// through LDS (the intra-block split-K of the TileScale README's GEMM
+// example, section "Example of GEMM"); each workgroup owns 16*NT columns.
+// Groups are loaded UNR at a time, double-buffered: the loads of the next
+// batch are in flight while this batch is dequantised and multiplied.
+// --------------------------------------------------------------------------
+template <int WAVES, int NT, int UNR>
+__global__ __launch_bounds__(WAVES * 64) void skinny_w4(TileArgs p)
+{
+    __shared__ float red[WAVES][NT][4][64];
+
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar offsets
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * NT);
+    const uint32_t row = lane & 15u, quarter = lane >> 4;
+    const int64_t KG = K / 128;  // K is a multiple of 128
+    const int64_t g0 = KG * wave / WAVES, g1 = KG * (wave + 1) / WAVES;
+    // Buffer loads with a fixed per-lane offset and the group's offset in the
+    // scalar operand; rows past M and columns past N read through an
+    // out-of-range offset, which returns zeros (no branches around the loads).
+    // The host guarantees every valid offset stays below 2^31.
+    const auto ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, kNumRecords, kBufferFlags);
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.qw + n0 * p.ldq), (short)0, kNumRecords, kBufferFlags);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.scales + n0 * p.lds), (short)0, kNumRecords, kBufferFlags);
+    // this lane's 64 bytes of A in group g: k = 128g + 32*quarter .. +31
+    const uint32_t va = (int64_t)row < M ? row * (uint32_t)p.lda * 2u + quarter * 64u : kOutOfRange;
+    uint32_t vq[NT], vs[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const bool ok = n0 + 16 * t + row < N;
+        vq[t] = ok ? (16u * t + row) * (uint32_t)p.ldq * 4u + quarter * 16u : kOutOfRange;
+        vs[t] = ok ? (16u * t + row) * (uint32_t)p.lds * 2u : kOutOfRange;
+    }
+    const W4Consts wc = w4_consts(p.zero_point);
+
+    // two accumulators per tile (even and odd MFMA of a group), so that
+    // consecutive MFMAs never wait on each other's result
+    f32x4 acc[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // loads of UNR groups starting at g (A chunks, int4 words, scales);
+    // groups at or past g1 read zeros through the out-of-range offset
+    auto load = [&](u32x4 (&a)[UNR][4], u32x4 (&q)[UNR][NT], uint32_t (&sc)[UNR][NT], int64_t g)
+                    __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int32_t gg = (int32_t)(g + u);
+            const uint32_t past = g + u < g1 ? 0u : kOutOfRange;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                a[u][j] = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(ra, (int)(va | past), gg * 256 + j * 16, 0));
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                q[u][t] = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rq, (int)(vq[t] | past), gg * 64, 0));
+                sc[u][t] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(vs[t] | past), gg * 2, 0);
+            }
+        }
+    };
+    auto compute = [&](u32x4 (&a)[UNR][4], u32x4 (&q)[UNR][NT], uint32_t (&sc)[UNR][NT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const _Float16 s = bit_cast<_Float16>((uint16_t)sc[u][t]);
+                    acc[t][j & 1] = Mfma16<E_F16>::run(a[u][j], dequant_w4_word(q[u][t][j], wc, f16x2{s, s}), acc[t][j & 1]);
+                }
+    };
+
+    // Batches of UNR groups in two register buffers, two batches per trip
+    // and no branch inside: the loads of one buffer are in flight while the
+    // other is dequantised and multiplied.  A batch wholly or partly past g1
+    // holds zeros (its products add nothing).
+    u32x4 a0[UNR][4], a1[UNR][4], q0[UNR][NT], q1[UNR][NT];
+    uint32_t s0[UNR][NT], s1[UNR][NT];  // one scale per register: nothing to pack after the loads
+    const int64_t nb = (g1 - g0 + UNR - 1) / UNR;
+    load(a0, q0, s0, g0);
+    for (int64_t b = 0; b < nb; b += 2) {
+        load(a1, q1, s1, g0 + (b + 1) * UNR);
+        __builtin_amdgcn_sched_barrier(0);  // these loads issue before the compute they hide behind
+        compute(a0, q0, s0);
+        __builtin_amdgcn_sched_barrier(0);
+        load(a0, q0, s0, g0 + (b + 2) * UNR);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(a1, q1, s1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    mfma_drain();
+    // partial tiles of this wave: value v of lane l is row 4*(l/16) + v, column l%16
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            red[wave][t][v][lane] = acc[t][0][v] + acc[t][1][v];
+    __syncthreads();
+    if (wave < NT) {  // wave t sums tile t over the K split, in wave order
+        const int t = (int)wave;
+        const int64_t col = n0 + 16 * t + row;
+        uint16_t* C = (uint16_t*)p.C;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float sum = red[0][t][v][lane];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w)
+                sum += red[w][t][v][lane];
+            const int64_t r = (int64_t)quarter * 4 + v;
+            if (r < M && col < N)
+                C[r * p.ldc + col] = convert_out<O_F16>(sum);
+        }
+    }
+}
+
 }  // namespace tg

@@ -57,6 +57,16 @@ bool w4_direct_eligible(const tg::TileArgs& a)
            128 * a.lds * 2 + a.K / 64 < lim;
 }
 
+// skinny_w4 addresses each operand through a buffer resource of kNumRecords
+// bytes (A from its first row, qweight and scales from the workgroup's first
+// column): every valid offset, per-lane part plus group part, must stay below
+// that bound.
+bool w4_skinny_eligible(const tg::TileArgs& a, int cols)
+{
+    const int64_t lim = (int64_t)tg::kNumRecords;
+    return a.M * a.lda * 2 + a.K * 2 < lim && cols * a.ldq * 4 + a.K / 2 < lim && cols * a.lds * 2 + a.K / 64 < lim;
+}
+
 }  // namespace
 
 extern "C" tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -97,6 +107,14 @@ extern "C" tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* 
     a.lds = lds;
     a.zero_point = zero_point;
     hipStream_t s = (hipStream_t)stream;
+    constexpr int WAVES = 8, NT = 2, UNR = 1;  // decode kernel: 16*NT columns per workgroup
+    if (M <= 16 && w4_skinny_eligible(a, 16 * NT)) {  // decode: a weight stream, too few output tiles
+        const int64_t blocks = (N + 16 * NT - 1) / (16 * NT);
+        if (blocks > 0x7FFFFFFF)
+            return TG_ERR_NOT_SUPPORTED;
+        hipLaunchKernelGGL((tg::skinny_w4<WAVES, NT, UNR>), dim3((uint32_t)blocks), dim3(WAVES * 64), 0, s, a);
+        return tg::launched();
+    }
     if (w4_direct_eligible(a)) {
         constexpr int BM = 64, BN = 128, NA = 4;
         const int64_t tiles = tg::n_tiles<BM, BN>(M, N);
