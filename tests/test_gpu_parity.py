@@ -254,11 +254,17 @@ def test_w4a16_layouts(tg, case):
     assert ok, (case, r, idx)
 
 
-# M <= 16: the decode kernel (eight waves split the 128-K groups; a group
-# count below, equal to and not a multiple of the wave count, batches of two
-# groups plus a tail), ragged N, every zero point at the ends of its range
+# M <= 16: the decode kernels.  K a multiple of 2048 (M <= 4, eight waves)
+# or 1024 (M > 4, four waves) takes the LDS-ring kernel (one instantiation
+# per A copy count: M <= 2, 4, 8, 16; a single stage per wave and several);
+# other K the register kernel (eight waves split the 128-K groups: a group
+# count below, equal to and not a multiple of the wave count).  Ragged N,
+# both ends of the zero-point range.
 @pytest.mark.parametrize("shape", [(1, 8, 128), (2, 40, 384), (7, 100, 1152), (16, 33, 256),
-                                   (16, 520, 2176), (5, 64, 1024), (1, 1000, 4096)],
+                                   (16, 520, 2176), (5, 64, 1024), (1, 1000, 4096),
+                                   (2, 72, 2048), (3, 33, 3072), (8, 100, 1024), (9, 64, 2048),
+                                   (16, 520, 1024), (16, 40, 8192), (4, 31, 5120), (3, 33, 6144),
+                                   (4, 100, 2048)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("zp", [0, 15])
 def test_w4a16_decode(tg, shape, zp):
@@ -293,6 +299,23 @@ def test_w4a16_decode_layouts_and_k0(tg):
     tg.tg_gemm_w4a16(A0, q0, s0, C)
     torch.cuda.synchronize()
     assert torch.all(C == 0) and torch.isnan(Cbuf[:, N:]).all()
+
+
+# the LDS-ring decode kernel with row strides above the minimum on every
+# operand (even scale stride, 4-byte-aligned scales)
+def test_w4a16_decode_lds_strided(tg):
+    M, N, K = 13, 96, 2048
+    A, q, s = _w4_inputs(M, N, K, seed=47)
+    sd = _gpu_strided(s, 2)
+    assert sd.stride(0) % 2 == 0 and sd.data_ptr() % 4 == 0
+    Cbuf = torch.full((M, N + 8), float("nan"), dtype=torch.float16, device="cuda")
+    C = Cbuf[:, :N]
+    tg.tg_gemm_w4a16(_gpu_strided(A, 56), _gpu_strided(q, 12), sd, C)
+    torch.cuda.synchronize()
+    cref, S = oracle.w4a16(A, q, s, K)
+    ok, r, idx = ochk.check(_f64(C), cref, S, K, "f16")
+    assert ok, (r, idx)
+    assert torch.isnan(Cbuf[:, N:]).all()
 
 
 @pytest.mark.parametrize("zp", [0, 8, 15])

@@ -435,4 +435,163 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4(TileArgs p)
     }
 }
 
+// --------------------------------------------------------------------------
+// The decode kernel with every operand copied to LDS (w4a16, M <= 16, K a
+// multiple of 1024, scales 4-byte aligned with an even stride).  The cost of
+// skinny_w4 is the texture-address work of its load instructions, not their
+// bytes: each 64-lane load takes the same address-unit time whether its
+// lanes fetch a 64-byte half line (the int4 words), a scattered 16 bytes of
+// A per row, or nothing (rows past M).  Here one copy instruction fetches
+// whole 128-byte lines -- 8 columns x 2 groups of int4 words, or 2 rows x 256
+// k of A -- and A needs only AI = ceil(M/2) of them per stage.
+//
+// Each wave owns a ring of RING LDS slots; a slot holds one stage of two
+// 128-K groups: 32 columns of int4 words (128 B each, 16-byte chunks XOR-
+// swizzled by column), 2*AI rows of A (512 B each, chunks swizzled by row;
+// lanes of rows past 2*AI read a zeroed 16-byte block instead) and the
+// stage's 64 scales.  The copies of stage s+RING-1 are issued before stage s
+// is computed, so RING-1 stages are in flight behind the compute; a wave
+// waits only for its own copies (no barrier in the loop).  The K order
+// inside each MFMA is that of skinny_w4 (a lane's four words and its A
+// chunks cover the same 32 k).
+// --------------------------------------------------------------------------
+constexpr int kW4dCols = 32;
+template <int AI> struct W4dLayout {
+    static constexpr int QB = kW4dCols * 128, AB = 2 * AI * 512, SB = 256;
+    static constexpr int SLOT = QB + AB + SB;
+};
+
+template <int AI, int WAVES, int RING>
+__global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
+{
+    typedef W4dLayout<AI> L;
+    constexpr int SLOT = L::SLOT, QB = L::QB, AB = L::AB;
+    constexpr int PER = 4 + AI + 1;  // copy instructions per stage: words, A rows, scales
+    constexpr int ZERO = WAVES * RING * SLOT;  // 16 zero bytes shared by every wave
+    static_assert(ZERO + 16 <= 160 * 1024 && WAVES * 2 * 4 * 64 * 4 <= ZERO, "LDS");
+    static_assert(AI >= 1 && AI <= 8 && RING >= 2 && (RING - 1) * PER <= 63, "copy ring");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[ZERO + 16];
+
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t n0 = (int64_t)blockIdx.x * kW4dCols;
+    const int64_t KG = K / 128;  // a multiple of 2*WAVES: every wave gets whole stages
+    const int64_t g0 = KG * wave / WAVES, nst = KG / (2 * WAVES);
+    uint8_t* ring = lds + wave * (RING * SLOT);
+    if (tid == 0)
+        *(u32x4*)(lds + ZERO) = u32x4{0u, 0u, 0u, 0u};
+
+    const i32x4_t ra = make_rsrc(p.A);
+    const i32x4_t rq = make_rsrc(p.qw + n0 * p.ldq);
+    const i32x4_t rs = make_rsrc(p.scales + n0 * p.lds);
+    // copy lanes: words -- instruction i, column 8i + lane/8, physical chunk
+    // lane%8 holding logical chunk (lane%8) ^ ((column/2)%8); A -- instruction
+    // i, row 2i + lane/32, physical chunk lane%32 holding logical chunk
+    // (lane%32) ^ row; scales -- lane l < 32 takes the two of column l
+    uint32_t vq[4], va[AI];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t col = 8u * i + lane / 8u;
+        const uint32_t chunk = (lane % 8u) ^ ((col >> 1) & 7u);
+        vq[i] = n0 + col < N ? col * (uint32_t)p.ldq * 4u + chunk * 16u : kOutOfRange;
+    }
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+        const uint32_t row = 2u * i + lane / 32u;
+        const uint32_t chunk = (lane % 32u) ^ row;
+        va[i] = (int64_t)row < M ? row * (uint32_t)p.lda * 2u + chunk * 16u : kOutOfRange;
+    }
+    const uint32_t vs = (lane < 32u && n0 + lane < N) ? lane * (uint32_t)p.lds * 2u : kOutOfRange;
+
+    // stage st of this wave (groups g0 + 2st, +1) into ring slot `slot`;
+    // a stage past the last one reads zeros (out-of-range offsets)
+    auto issue = [&](int64_t st, uint8_t* slot) __attribute__((always_inline)) {
+        const uint32_t past = st < nst ? 0u : kOutOfRange;
+        const uint32_t g = (uint32_t)(g0 + 2 * st);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            load_lds_1k(rq, slot + i * 1024, vq[i] | past, g * 64u);
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+            load_lds_1k(ra, slot + QB + i * 1024, va[i] | past, g * 256u);
+        load_lds_256(rs, slot + QB + AB, vs | past, g * 2u);
+    };
+
+    const W4Consts wc = w4_consts(p.zero_point);
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t c = lane & 15u, h = lane >> 4;  // MFMA lane: column (or row) c, quarter h
+    const bool arow = c < 2u * AI;                  // this lane's A row is held in the slot
+
+    auto compute = [&](const uint8_t* slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            u32x4 q[2];
+            _Float16 sc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t col = 16u * t + c;
+                const uint32_t phys = (4u * u + h) ^ ((col >> 1) & 7u);
+                q[t] = lds128(slot, col * 128u + phys * 16u);
+                sc[t] = bit_cast<_Float16>(*(const uint16_t*)(slot + QB + AB + col * 4u + u * 2u));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t phys = (16u * u + 4u * h + j) ^ c;
+                const u32x4 a = lds128(lds, arow ? (uint32_t)(slot - lds) + QB + c * 512u + phys * 16u : (uint32_t)ZERO);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    acc[t][j & 1] = Mfma16<E_F16>::run(a, dequant_w4_word(q[t][j], wc, f16x2{sc[t], sc[t]}), acc[t][j & 1]);
+            }
+        }
+    };
+
+    __syncthreads();  // the zero block is written
+    if (nst > 0) {
+#pragma unroll
+        for (int r = 0; r < RING - 1; ++r)
+            issue(r, ring + r * SLOT);
+        uint32_t cur = 0;  // slot of stage st
+        for (int64_t st = 0; st < nst; ++st) {
+            const uint32_t nxt = cur >= 1 ? cur - 1 : RING - 1;  // slot of stage st+RING-1 == slot of st-1
+            issue(st + RING - 1, ring + nxt * SLOT);
+            wait_copies<(RING - 1) * PER>();  // this wave's copies of stage st have landed
+            __builtin_amdgcn_sched_barrier(0);
+            compute(ring + cur * SLOT);
+            __builtin_amdgcn_sched_barrier(0);
+            cur = cur + 1 == RING ? 0 : cur + 1;
+        }
+    }
+    wait_copies<0>();  // the trailing zero stages land before LDS is reused
+    mfma_drain();
+
+    // partial tiles: value v of lane l is row 4*(l/16) + v, column l%16
+    __syncthreads();
+    float* red = (float*)lds;  // [wave][tile][v][lane]
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            red[((wave * 2 + t) * 4 + v) * 64 + lane] = acc[t][0][v] + acc[t][1][v];
+    __syncthreads();
+    if (wave < 2) {  // wave t sums tile t over the K split, in wave order
+        const int t = (int)wave;
+        const int64_t col = n0 + 16 * t + c;
+        uint16_t* C = (uint16_t*)p.C;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float sum = red[(t * 4 + v) * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w)
+                sum += red[((w * 2 + t) * 4 + v) * 64 + lane];
+            const int64_t r = (int64_t)h * 4 + v;
+            if (r < M && col < N)
+                C[r * p.ldc + col] = convert_out<O_F16>(sum);
+        }
+    }
+}
+
 }  // namespace tg

@@ -67,6 +67,53 @@ bool w4_skinny_eligible(const tg::TileArgs& a, int cols)
     return a.M * a.lda * 2 + a.K * 2 < lim && cols * a.ldq * 4 + a.K / 2 < lim && cols * a.lds * 2 + a.K / 64 < lim;
 }
 
+// skinny_w4_lds: whole stages of two scale groups per wave (K a multiple of
+// 2 * 128 * waves), scales copied as aligned 4-byte pairs, and the same
+// buffer-offset bound as skinny_w4 for its 16 A rows and 32 columns.
+bool w4_skinny_lds_eligible(const tg::TileArgs& a, int waves)
+{
+    if (a.K <= 0 || a.K % (256 * waves) != 0 || ((uintptr_t)a.scales & 3u) != 0 || (a.lds & 1) != 0)
+        return false;
+    const int64_t lim = (int64_t)tg::kNumRecords;
+    return 16 * a.lda * 2 + a.K * 2 < lim && tg::kW4dCols * a.ldq * 4 + a.K / 2 < lim &&
+           tg::kW4dCols * a.lds * 2 + a.K / 64 < lim;
+}
+
+// ring depth: as many slots as fit the LDS with WAVES waves
+template <int AI, int WAVES>
+constexpr int w4d_ring()
+{
+    constexpr int r = (160 * 1024 - 16) / (WAVES * tg::W4dLayout<AI>::SLOT);
+    constexpr int rmax = 63 / (4 + AI + 1) + 1;
+    return r < rmax ? r : rmax;
+}
+
+// eight waves (two per SIMD) where the LDS still holds three slots for each,
+// else four with a deeper ring
+template <int AI>
+constexpr int w4d_waves()
+{
+    return w4d_ring<AI, 8>() >= 3 ? 8 : 4;
+}
+
+// launches the LDS decode kernel for AI A-copy instructions per stage, or
+// returns false (nothing launched) if the problem does not fit its shape
+template <int AI>
+bool launch_skinny_lds(const tg::TileArgs& a, hipStream_t s, tg_status* st)
+{
+    constexpr int WAVES = w4d_waves<AI>(), RING = w4d_ring<AI, WAVES>();
+    if (!w4_skinny_lds_eligible(a, WAVES))
+        return false;
+    const int64_t blocks = (a.N + tg::kW4dCols - 1) / tg::kW4dCols;
+    if (blocks > 0x7FFFFFFF) {
+        *st = TG_ERR_NOT_SUPPORTED;
+        return true;
+    }
+    hipLaunchKernelGGL((tg::skinny_w4_lds<AI, WAVES, RING>), dim3((uint32_t)blocks), dim3(WAVES * 64), 0, s, a);
+    *st = tg::launched();
+    return true;
+}
+
 }  // namespace
 
 extern "C" tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -107,6 +154,12 @@ extern "C" tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* 
     a.lds = lds;
     a.zero_point = zero_point;
     hipStream_t s = (hipStream_t)stream;
+    if (M <= 16) {  // decode: a weight stream, too few output tiles to fill the chip
+        tg_status lst = TG_OK;
+        if ((M <= 2 && launch_skinny_lds<1>(a, s, &lst)) || (M > 2 && M <= 4 && launch_skinny_lds<2>(a, s, &lst)) ||
+            (M > 4 && M <= 8 && launch_skinny_lds<4>(a, s, &lst)) || (M > 8 && launch_skinny_lds<8>(a, s, &lst)))
+            return lst;
+    }
     constexpr int WAVES = 8, NT = 2, UNR = 1;  // decode kernel: 16*NT columns per workgroup
     if (M <= 16 && w4_skinny_eligible(a, 16 * NT)) {  // decode: a weight stream, too few output tiles
         const int64_t blocks = (N + 16 * NT - 1) / (16 * NT);
