@@ -71,6 +71,16 @@ __device__ __forceinline__ void load_lds_1k(i32x4_t r, uint8_t* dst, uint32_t vo
                  : "memory");
 }
 
+// As load_lds_1k, with the destination given as an LDS address (wave-uniform):
+// no pointer conversion in the hot loop.
+__device__ __forceinline__ void load_lds_1k_at(i32x4_t r, uint32_t dst, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(soff), "{m0}"(dst)
+                 : "memory");
+}
+
 // wait until at most N of this wave's copies are outstanding (they retire in order)
 template <int N>
 __device__ __forceinline__ void wait_copies()
@@ -157,24 +167,39 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         const uint32_t kmax = kleft >= KE ? (uint32_t)KE : (uint32_t)kleft;
         return (lchunk * CE < kmax) ? 0u : kOutOfRange;
     };
-    // copy instruction j of operand A (or B) for K step kt into its stage; a
-    // step past the last one reads through the out-of-range offset, which only
-    // writes zeros into a stage buffer that is not read again
-    auto copy_a = [&](auto edge, int64_t kt, int j) __attribute__((always_inline)) {
-        uint32_t v = (j & 1) ? (va1 | chunk_oob(kt, lchunk1)) : (va0 | chunk_oob(kt, lchunk0));
-        v |= kt < KT ? 0u : kOutOfRange;
-        if constexpr (decltype(edge)::value)
-            v |= (int32_t)(wave * (BM / NW) + RPI * j + lrowi) < rows_a ? 0u : kOutOfRange;
-        load_lds_1k(ra, a_ptr(kt) + wave * (BM / NW) * RB + j * 1024, v,
-                    (uint32_t)kt * RB + (uint32_t)(RPI * j) * ldab);
+    // Per-lane offsets of the copies of half-stage h (o0 for even copy
+    // instructions, o1 for odd ones), computed once per half-stage.  A step
+    // past the last one reads through the out-of-range offset (zeros, into a
+    // stage buffer that is not read again).  The K tail is checked only on
+    // the edge path: the full-tile path runs with K a multiple of KE.
+    auto half_offs = [&](auto edge, int64_t h, uint32_t& o0, uint32_t& o1) __attribute__((always_inline)) {
+        const int64_t kt = h >> 1;
+        o0 = (h & 1) ? vb0 : va0;
+        o1 = (h & 1) ? vb1 : va1;
+        if constexpr (decltype(edge)::value) {
+            o0 |= chunk_oob(kt, lchunk0);
+            o1 |= chunk_oob(kt, lchunk1);
+        }
+        const uint32_t past = kt < KT ? 0u : kOutOfRange;
+        o0 |= past;
+        o1 |= past;
     };
-    auto copy_b = [&](auto edge, int64_t kt, int j) __attribute__((always_inline)) {
-        uint32_t v = (j & 1) ? (vb1 | chunk_oob(kt, lchunk1)) : (vb0 | chunk_oob(kt, lchunk0));
-        v |= kt < KT ? 0u : kOutOfRange;
-        if constexpr (decltype(edge)::value)
-            v |= (int32_t)(wave * (BN / NW) + RPI * j + lrowi) < rows_b ? 0u : kOutOfRange;
-        load_lds_1k(rb, b_ptr(kt) + wave * (BN / NW) * RB + j * 1024, v,
-                    (uint32_t)kt * RB + (uint32_t)(RPI * j) * ldbb);
+    // LDS address of this wave's rows in half-stage h
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+    auto half_dst = [&](int64_t h) __attribute__((always_inline)) -> uint32_t {
+        return lds0 + (uint32_t)(h % NH) * HALF + wave * ((h & 1) ? BN / NW : BM / NW) * RB;
+    };
+    // copy instruction q of half-stage h (A of step h/2 for even h, B for odd
+    // h), with the offsets o0/o1 of that half-stage
+    auto copy_half = [&](auto edge, int64_t h, int q, uint32_t o0, uint32_t o1) __attribute__((always_inline)) {
+        const int64_t kt = h >> 1;
+        uint32_t v = (q & 1) ? o1 : o0;
+        if constexpr (decltype(edge)::value) {
+            const int32_t rows = (h & 1) ? rows_b : rows_a;
+            v |= (int32_t)(wave * ((h & 1) ? BN / NW : BM / NW) + RPI * q + lrowi) < rows ? 0u : kOutOfRange;
+        }
+        load_lds_1k_at((h & 1) ? rb : ra, half_dst(h) + q * 1024, v,
+                       (uint32_t)kt * RB + (uint32_t)(RPI * q) * ((h & 1) ? ldbb : ldab));
     };
 
     // ---- fragment reads: every fragment row of this lane has the same swz(row)
@@ -250,14 +275,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     };
     auto nothing = [](int) {};
 
-    // copy instruction q of half-stage h (A of step h/2 for even h, B for odd h)
-    auto copy_half = [&](auto edge, int64_t h, int q) __attribute__((always_inline)) {
-        if ((h & 1) == 0)
-            copy_a(edge, h >> 1, q);
-        else
-            copy_b(edge, h >> 1, q);
-    };
-
     // One K step.  Entering, the fragments of its sub-step 0 are in slot 0.
     // Half-stage 2kt+NH-1 (whose slot was freed by the previous barrier) is
     // copied during sub-step 0.  The barrier before the last sub-step
@@ -265,11 +282,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     // frees the two half-stages of step kt: half-stage 2kt+NH is copied during
     // the last sub-step, while the first fragments of step kt+1 are read.
     auto step = [&](auto edge, int64_t kt) __attribute__((always_inline)) {
+        uint32_t p0, p1, r0, r1;
+        half_offs(edge, 2 * kt + NH - 1, p0, p1);
+        half_offs(edge, 2 * kt + NH, r0, r1);
 #pragma unroll
         for (int s = 0; s < KSTEPS - 1; ++s) {
             auto rd = [&](int r) __attribute__((always_inline)) { read_frag(kt, s + 1, (s + 1) & 1, r); };
             if (s == 0)
-                substep(s & 1, rd, [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH - 1, q); },
+                substep(s & 1, rd,
+                        [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH - 1, q, p0, p1); },
                         std::integral_constant<int, AI>{});
             else
                 substep(s & 1, rd, nothing, std::integral_constant<int, 0>{});
@@ -280,17 +301,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         __builtin_amdgcn_sched_barrier(0);
         // (the reads of step kt+1 after the last step are stale and unused)
         substep((KSTEPS - 1) & 1, [&](int r) __attribute__((always_inline)) { read_frag(kt + 1, 0, 0, r); },
-                [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH, q); },
+                [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH, q, r0, r1); },
                 std::integral_constant<int, AI>{});
     };
 
     auto run = [&](auto edge) __attribute__((always_inline)) {
         // half-stages 0 .. NH-2
 #pragma unroll
-        for (int h = 0; h < NH - 1; ++h)
+        for (int h = 0; h < NH - 1; ++h) {
+            uint32_t o0, o1;
+            half_offs(edge, h, o0, o1);
 #pragma unroll
             for (int j = 0; j < AI; ++j)
-                copy_half(edge, h, j);
+                copy_half(edge, h, j, o0, o1);
+        }
         wait_copies<(NH - 3) * AI>();  // step 0 landed
         __syncthreads();
         read_frags(0, 0, 0);
@@ -299,7 +323,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         wait_copies<0>();  // copies past the last step (zeros) must land before LDS is reused
     };
     if (KT > 0) {
-        if (rows_a == BM && rows_b == BN)
+        if (rows_a == BM && rows_b == BN && K % KE == 0)  // full tiles, no K tail
             run(std::false_type{});
         else
             run(std::true_type{});
