@@ -13,8 +13,9 @@ Printed: ONE JSON line with the metric, `roofline` (the GEMM kernel's
 achieved TFLOP/s against the dense bf16 MFMA peak, from HIP events around
 each launch inside the timed region), `cpu_baseline` (the CPU oracle timed
 on a bounded sample of the same workload) and `secondary` (the skinny M=16
-GEMM's GB/s against the HBM peak, the fp8 and w4a16 workloads, and the
-w4a16 weights at decode batch sizes M=16 and M=1), each
+GEMM's GB/s against the HBM peak, the same GEMM on an 8-way column shard
+(N=1024), the fp8 and w4a16 workloads, and the w4a16 weights at decode batch
+sizes M=16 and M=1), each
 secondary timed launch by launch with the 256 MB Infinity Cache flushed
 (by a 512 MiB read) before every launch.
 """
@@ -128,6 +129,21 @@ def setup_skinny():
     return w, fn, flops, bytes_
 
 
+def setup_skinny_shard():
+    """The skinny workload's 8-way column shard: M=16, N=1024, K=8192."""
+    import torch
+    import synth
+    import tile_level_gemm_02_amd as tg
+
+    w = synth.workload("bf16_skinny", N=1024)
+    A, B = w["A"].cuda(), w["B"].cuda()
+    C = torch.empty((w["M"], w["N"]), dtype=torch.float32, device="cuda")
+    fn = lambda: tg.tg_gemm_bf16(A, B, C, b_layout="col")
+    flops = 2.0 * w["M"] * w["N"] * w["K"]
+    bytes_ = 2 * (w["M"] * w["K"] + w["N"] * w["K"]) + 4 * w["M"] * w["N"]
+    return w, fn, flops, bytes_
+
+
 def setup_fp8():
     import torch
     import synth
@@ -196,7 +212,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (to scale HBM byte counters)")
-    ap.add_argument("--only", choices=["bf16_4096", "bf16_skinny", "fp8_8192", "w4a16", "w4a16_m16", "w4a16_m1"],
+    ap.add_argument("--only", choices=["bf16_4096", "bf16_skinny", "bf16_skinny_n1024", "fp8_8192", "w4a16", "w4a16_m16",
+                                       "w4a16_m1"],
                     default=None,
                     help="only run this workload's launches (for counter collection), no JSON line")
     args = ap.parse_args()
@@ -224,7 +241,8 @@ def main():
         return
     flush = make_flush()
     if args.only:
-        setup = {"bf16_4096": setup_bf16_4096, "bf16_skinny": setup_skinny, "fp8_8192": setup_fp8,
+        setup = {"bf16_4096": setup_bf16_4096, "bf16_skinny": setup_skinny, "bf16_skinny_n1024": setup_skinny_shard,
+                 "fp8_8192": setup_fp8,
                  "w4a16": setup_w4a16, "w4a16_m16": lambda: setup_w4a16(16),
                  "w4a16_m1": lambda: setup_w4a16(1)}[args.only]
         _, fn, _, _ = setup()
@@ -283,7 +301,8 @@ def main():
     if not args.no_secondary:
         sec = {}
         n = max(10, min(args.steps, 50))
-        for name, setup, peak_key in (("bf16_skinny", setup_skinny, "hbm"), ("fp8_8192", setup_fp8, "fp8"),
+        for name, setup, peak_key in (("bf16_skinny", setup_skinny, "hbm"), ("bf16_skinny_n1024", setup_skinny_shard, "hbm"),
+                                      ("fp8_8192", setup_fp8, "fp8"),
                                       ("w4a16", setup_w4a16, "both"),
                                       ("w4a16_m16", lambda: setup_w4a16(16), "hbm"),
                                       ("w4a16_m1", lambda: setup_w4a16(1), "hbm")):

@@ -122,6 +122,37 @@ def test_skinny_ragged(tg, dt, M):
     _check(C, A, B, dt, "col", "f32")
 
 
+# Narrow N with fp32 output (a column shard of the skinny workload): the
+# skinny kernel also splits K over workgroups and adds their partial tiles
+# into a zeroed C with fp32 atomics.  Ragged N and K, a split count that does
+# not divide the K blocks, a K tail inside the last split, and K too short
+# to split.
+@pytest.mark.parametrize("shape", [(16, 1024, 8192), (5, 512, 4104), (1, 64, 2048), (16, 1000, 1000),
+                                   (3, 40, 8200), (16, 33, 30000)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_skinny_split_k(tg, dt, shape):
+    M, N, K = shape
+    A, B, _, _ = _inputs(dt, M, N, K, "col", seed=N + K + M)
+    C = _run_dense(tg, dt, A, B, "col", "f32")
+    _check(C, A, B, dt, "col", "f32")
+
+
+def test_skinny_split_k_leaves_padding(tg):
+    """The split path zeroes and adds into C's M x N entries only; columns past N
+    in a padded row are left alone, and a second call gives the same result."""
+    M, N, K = 9, 200, 6144
+    A, B, _, _ = _inputs("bf16", M, N, K, "col", seed=91)
+    store = torch.full((M, N + 24), 5.0, dtype=torch.float32, device="cuda")
+    C = store[:, :N]
+    _run_dense(tg, "bf16", A, B, "col", "f32", C=C)
+    first = C.clone()
+    _run_dense(tg, "bf16", A, B, "col", "f32", C=C)
+    assert torch.all(store[:, N:] == 5.0)
+    _check(C, A, B, "bf16", "col", "f32")
+    # partial tiles add in any order: a repeat agrees within the bound, not bit for bit
+    _check(first, A, B, "bf16", "col", "f32")
+
+
 @pytest.mark.parametrize("dt,lay", [("bf16", "col"), ("f16", "row"), ("fp8", "col")])
 def test_medium_multi_tile(tg, dt, lay):
     """Sizes that select the 128 and 256 tiles, ragged on M and N."""

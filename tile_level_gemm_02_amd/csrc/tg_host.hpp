@@ -158,6 +158,18 @@ tg_status launch_dense(TileArgs& a, int c_dtype, hipStream_t s)
     }
 }
 
+// Workgroups per column block of the skinny kernel: enough for 256 CUs when
+// N alone gives fewer, keeping at least four 32-wide K blocks per wave.
+inline int skinny_split(int64_t blocks, int64_t K)
+{
+    const int64_t kb = (K + 31) / 32;
+    int64_t split = (256 + blocks - 1) / blocks;
+    const int64_t most = kb / (8 * 4);
+    if (split > most)
+        split = most;
+    return split > 1 ? (int)split : 1;
+}
+
 // fp16 / bf16 GEMM.  M <= 16 against a K-contiguous B takes the skinny
 // kernel; everything else the tile kernel (K == 0 runs it with no K steps,
 // which stores zeros: the empty sum).
@@ -176,6 +188,15 @@ tg_status gemm_16bit(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
         const int64_t blocks = (N + 16 * NT - 1) / (16 * NT);
         if (blocks > 0x7FFFFFFF)
             return TG_ERR_NOT_SUPPORTED;
+        const int split = skinny_split(blocks, K);
+        if (split > 1 && c_dtype == TG_F32) {  // narrow N: split K over workgroups too
+            const int64_t total = M * N;
+            const int64_t zb = (total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024;
+            hipLaunchKernelGGL(zero_f32<>, dim3((uint32_t)zb), dim3(256), 0, s, (float*)C, M, N, ldc);
+            hipLaunchKernelGGL((skinny_gemm<E, O_F32, 8, NT, UNR, true>), dim3((uint32_t)blocks, (uint32_t)split),
+                               dim3(512), 0, s, sa);
+            return launched();
+        }
         switch (c_dtype) {
         case TG_F32:
             hipLaunchKernelGGL((skinny_gemm<E, O_F32, 8, NT, UNR>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);

@@ -319,10 +319,15 @@ template <> struct Mfma16<E_BF16> {
     }
 };
 
-template <int E, int O, int WAVES, int NT, int UNR>
+// SPLIT: the K blocks are also split over gridDim.y workgroups per column
+// block (for narrow N, where N / (16*NT) workgroups leave most CUs idle);
+// each adds its partial tile into the fp32 output, which the host has zeroed
+// (fp32 atomic adds, so the summation order over the split is not fixed).
+template <int E, int O, int WAVES, int NT, int UNR, bool SPLIT = false>
 __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
 {
     typedef typename OutInfo<O>::T OutT;
+    static_assert(!SPLIT || O == O_F32, "partial tiles are added in fp32");
     __shared__ float red[WAVES][NT][4][64];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
@@ -331,7 +336,10 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
     const int64_t row = lane & 15u;
     const int64_t koff = (int64_t)(lane >> 4) * 8;  // element offset inside a 32-wide K block
     const int64_t KB = (K + 31) / 32;
-    const int64_t kb0 = KB * wave / WAVES, kb1 = KB * (wave + 1) / WAVES;
+    // this workgroup's K blocks [z0, z1), split over its waves
+    const int64_t z0 = SPLIT ? KB * blockIdx.y / gridDim.y : 0;
+    const int64_t z1 = SPLIT ? KB * (blockIdx.y + 1) / gridDim.y : KB;
+    const int64_t kb0 = z0 + (z1 - z0) * wave / WAVES, kb1 = z0 + (z1 - z0) * (wave + 1) / WAVES;
     const bool rok = row < M;
     const uint8_t* aptr = p.A + (rok ? row : 0) * p.lda * 2;
     bool cok[NT];
@@ -418,10 +426,25 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
             for (int w = 1; w < WAVES; ++w)
                 s += red[w][t][v][lane];
             const int64_t r = (int64_t)(lane >> 4) * 4 + v;
-            if (r < M && col < N)
-                C[r * p.ldc + col] = convert_out<O>(s);
+            if (r < M && col < N) {
+                if constexpr (SPLIT)
+                    atomicAdd((float*)p.C + r * p.ldc + col, s);
+                else
+                    C[r * p.ldc + col] = convert_out<O>(s);
+            }
         }
     }
+}
+
+// Zero an M x N fp32 matrix with leading dimension ldc (the split skinny
+// GEMM adds its partial tiles into it).  A template only so that every
+// translation unit that launches it may define it.
+template <int = 0>
+__global__ __launch_bounds__(256) void zero_f32(float* C, int64_t M, int64_t N, int64_t ldc)
+{
+    const int64_t total = M * N;
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256)
+        C[(t / N) * ldc + t % N] = 0.0f;
 }
 
 // --------------------------------------------------------------------------
