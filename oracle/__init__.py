@@ -1,4 +1,4 @@
-"""CPU oracle for the tile GEMM and the w4a16 dequant GEMM.
+"""CPU oracle for the tile GEMM, the w4a16 dequant GEMM and the 2:4 sparse GEMM.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The product path
@@ -51,6 +51,8 @@ def _load():
         build(force=False)
         lib = ctypes.CDLL(_LIB)
         i64, i32, vp, dp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
+        lib.orc_expand_sp24.argtypes = [i64, i64, vp, i64, vp, i64, vp, i64]
+        lib.orc_expand_sp24.restype = ctypes.c_int
         lib.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.orc_f16_to_f64.restype = dp
         lib.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
@@ -186,6 +188,55 @@ def gemm(fmt: int, A, B, b_layout: int, scale_a: float = 1.0, scale_b: float = 1
     if rc != 0:
         raise MemoryError("oracle gemm: out of memory")
     return C, S
+
+
+# ------------------------------------------------------- 2:4 sparse weights
+
+def expand_sp24(vals, meta, K: int) -> np.ndarray:
+    """bf16 (or fp16) bits W[N][K] of 2:4-compressed weights (format in oracle.c).
+
+    ``vals`` 16-bit [N][K/2] (the kept values of each group of 4, in position
+    order), ``meta`` uint8 [N][K/8] (a 4-bit code i0 | i1 << 2 per group, low
+    nibble first).  Raises ValueError on a code with i0 >= i1.
+    """
+    lib = _load()
+    v = _bits(vals, 2)
+    m = np.ascontiguousarray(meta.numpy() if hasattr(meta, "numpy") else meta, dtype=np.uint8)
+    N = v.shape[0]
+    assert K % 4 == 0 and v.shape[1] >= K // 2 and m.shape[1] >= (K + 7) // 8 and m.shape[0] == N
+    W = np.empty((N, K), dtype=np.uint16)
+    if lib.orc_expand_sp24(N, K, _ptr(v), v.shape[1], _ptr(m), m.shape[1], _ptr(W), K) != 0:
+        raise ValueError("2:4 metadata: a group code with i0 >= i1")
+    return W
+
+
+def compress_sp24(W_bits) -> tuple:
+    """(vals, meta) of an N x K matrix of 16-bit element bits whose every group
+    of 4 along K has at most 2 nonzero entries (bits other than +-0); unused
+    slots take the lowest free positions.  Pure Python: small inputs only."""
+    W = np.asarray(_bits(W_bits, 2))
+    N, K = W.shape
+    vals = np.zeros((N, K // 2), dtype=np.uint16)
+    meta = np.zeros((N, (K + 7) // 8), dtype=np.uint8)
+    for n in range(N):
+        for g in range(K // 4):
+            grp = W[n, 4 * g: 4 * g + 4]
+            keep = [j for j in range(4) if grp[j] & 0x7FFF]
+            if len(keep) > 2:
+                raise ValueError(f"row {n} group {g}: more than 2 nonzeros")
+            for j in range(4):
+                if len(keep) < 2 and j not in keep:
+                    keep.append(j)
+            i0, i1 = sorted(keep[:2])
+            vals[n, 2 * g], vals[n, 2 * g + 1] = grp[i0], grp[i1]
+            meta[n, g // 2] |= (i0 | (i1 << 2)) << (4 * (g % 2))
+    return vals, meta
+
+
+def gemm_sp24(A, vals, meta, K: int, fmt: int = BF16, nthreads: int | None = None):
+    """C, S for C = A . W^T with W the expanded 2:4 weights (N x K, K-contiguous)."""
+    W = expand_sp24(vals, meta, K)
+    return gemm(fmt, A, W, B_NK, nthreads=nthreads)
 
 
 def w4a16(A, qweight, scales, K: int, group_size: int = 128, zero_point: int = 8,

@@ -218,6 +218,38 @@ void orc_dequant_w4(int64_t N, int64_t K, const int32_t *qweight, int64_t ldq,
     }
 }
 
+/* --------------------------------------------------- 2:4 sparse weights */
+
+/* Structured 2:4 sparsity along K of an N x K weight matrix (the sparse
+ * GEMM T.gemm_sp that "TileScale 与 TileLang比较" lists in its timeline of
+ * TileLang features; the page gives no storage format, so this one is a
+ * reading): every aligned group of 4 consecutive k of a row keeps at most 2
+ * entries.  Row n is stored as
+ *   vals[n*ldv + 2g], vals[n*ldv + 2g + 1]  -- the 2 kept values of group g,
+ *   code(n, g) = (meta[n*ldm + g/2] >> (4*(g%2))) & 0xF,  i0 = code & 3,
+ *   i1 = code >> 2, with i0 < i1  -- their positions k = 4g + i0, 4g + i1.
+ * A group with fewer than 2 nonzero entries keeps zeros in unused slots.
+ * W[n*ldw + k] receives the element bits unchanged; the other two positions
+ * of each group are zero.  Returns -1 (W partly written) at the first code
+ * with i0 >= i1, else 0.  K must be a multiple of 4. */
+int orc_expand_sp24(int64_t N, int64_t K, const uint16_t *vals, int64_t ldv,
+                    const uint8_t *meta, int64_t ldm, uint16_t *W, int64_t ldw)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < K / 4; ++g) {
+            int code = (meta[n * ldm + g / 2] >> (4 * (g % 2))) & 0xF;
+            int i0 = code & 3, i1 = code >> 2;
+            if (i0 >= i1)
+                return -1;
+            for (int j = 0; j < 4; ++j)
+                W[n * ldw + 4 * g + j] = 0;
+            W[n * ldw + 4 * g + i0] = vals[n * ldv + 2 * g];
+            W[n * ldw + 4 * g + i1] = vals[n * ldv + 2 * g + 1];
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------- GEMM */
 
 /* Naive triple loop straight from the stored bits, single-threaded.  The

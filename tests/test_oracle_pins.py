@@ -11,7 +11,11 @@ or group index) fails at least one of them:
   triple loop;
 * int4 dequant: hand-worked words and a worked rounding case (tests/golden),
   exhaustive over every positive finite fp16 scale against numpy's correctly
-  rounded binary64 -> binary16 conversion, a closed form for the group index.
+  rounded binary64 -> binary16 conversion, a closed form for the group index;
+* 2:4 sparse weights: hand-worked rows and dot products (tests/golden), every
+  valid group code against its position pair, rejection of invalid codes,
+  compress/expand round trips on random 2:4 matrices, closed forms for the
+  sparse GEMM, and planted mistakes (nibble order, value order) that fail.
 """
 from fractions import Fraction
 
@@ -356,3 +360,110 @@ def test_checker_bounds():
     assert not ok and r == np.inf
     ok, _, _ = ochk.check(np.array([[np.inf]]), cref, S, 50, "bf16")
     assert not ok
+
+
+# ------------------------------------------------------ 2:4 sparse weights
+
+def _sparse_golden():
+    rows, dots = [], []
+    import os
+    from _golden import GOLDEN
+    with open(os.path.join(GOLDEN, "sparse24_rows.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, rhs = line.split("->")
+            toks = lhs.split()
+            exp = [float(x) for x in rhs.split()]
+            if toks[0] == "row":
+                mi = toks.index("meta")
+                rows.append(([float(x) for x in toks[2:mi]], int(toks[mi + 1], 16), exp))
+            else:
+                dots.append(([float(x) for x in toks[2:]], exp))
+    return rows, dots
+
+
+def test_sparse24_golden_rows_and_dots():
+    rows, dots = _sparse_golden()
+    vals = np.stack([oracle.encode_bf16(np.array(v)) for v, _, _ in rows])
+    meta = np.array([[m] for _, m, _ in rows], dtype=np.uint8)
+    W = oracle.expand_sp24(vals, meta, 8)
+    for i, (_, _, exp) in enumerate(rows):
+        assert oracle.decode(oracle.BF16, W[i]).tolist() == exp
+    a, exp = dots[0]
+    A = _to_fmt([a], oracle.BF16)
+    C, _ = oracle.gemm_sp24(A, vals, meta, 8)
+    assert C[0].tolist() == exp
+
+
+def test_sparse24_every_code():
+    """Each of the 6 valid codes puts the two values at exactly its two positions."""
+    for i0 in range(4):
+        for i1 in range(i0 + 1, 4):
+            code = i0 | (i1 << 2)
+            vals = oracle.encode_bf16(np.array([[3.0, -5.0, 0.5, 9.0]]))
+            meta = np.array([[code | (code << 4)]], dtype=np.uint8)
+            d = oracle.decode(oracle.BF16, oracle.expand_sp24(vals, meta, 8)[0])
+            for g, (x, y) in enumerate(((3.0, -5.0), (0.5, 9.0))):
+                exp = [0.0] * 4
+                exp[i0], exp[i1] = x, y
+                assert d[4 * g: 4 * g + 4].tolist() == exp
+
+
+def test_sparse24_rejects_invalid_codes():
+    vals = np.zeros((1, 4), dtype=np.uint16)
+    for code in [i0 | (i1 << 2) for i0 in range(4) for i1 in range(4) if i0 >= i1]:
+        with pytest.raises(ValueError):
+            oracle.expand_sp24(vals, np.array([[code | (0xE << 4)]], dtype=np.uint8), 8)
+        with pytest.raises(ValueError):  # the high nibble (group 1) is checked too
+            oracle.expand_sp24(vals, np.array([[0xE | (code << 4)]], dtype=np.uint8), 8)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_sparse24_round_trip(seed):
+    """A random dense matrix with at most 2 nonzeros per group survives compress -> expand,
+    and every expanded group holds at most 2 nonzeros."""
+    rng = np.random.default_rng(seed)
+    N, K = 7, 48
+    dense = rng.standard_normal((N, K))
+    for n in range(N):
+        for g in range(K // 4):
+            drop = rng.choice(4, size=4 - rng.integers(0, 3), replace=False)
+            dense[n, 4 * g + drop] = 0.0
+    bits = oracle.encode_bf16(dense)
+    vals, meta = oracle.compress_sp24(bits)
+    back = oracle.expand_sp24(vals, meta, K)
+    assert np.array_equal(back, bits)
+    nz = (back.reshape(N, K // 4, 4) & 0x7FFF) != 0
+    assert nz.sum(axis=2).max() <= 2
+
+
+def test_sparse24_gemm_closed_forms():
+    """All-ones kept values: C = (number of groups) * 2 * a for a constant A row;
+    a one-hot A column picks out the expanded weight column."""
+    N, K = 5, 64
+    vals = oracle.encode_bf16(np.ones((N, K // 2)))
+    meta = np.full((N, K // 8), 0x9 | (0x9 << 4), dtype=np.uint8)  # code 0x9 = 1 | 2<<2: positions 1, 2
+    A = _to_fmt(np.full((3, K), 2.0), oracle.BF16)
+    C, S = oracle.gemm_sp24(A, vals, meta, K)
+    assert np.all(C == 2.0 * (K // 2)) and np.all(S == C)
+    for k in (0, 1, 2, 5, 6, 63):
+        a = np.zeros((1, K)); a[0, k] = 1.0
+        C, _ = oracle.gemm_sp24(_to_fmt(a, oracle.BF16), vals, meta, K)
+        assert np.all(C[0] == (1.0 if k % 4 in (1, 2) else 0.0))
+
+
+def test_planted_sparse24_mistakes_are_caught():
+    """Reading the high nibble first, or the two values of a group in reverse order,
+    fails the hand-worked rows."""
+    rows, _ = _sparse_golden()
+    v, m, exp = rows[0]
+    vals = oracle.encode_bf16(np.array([v]))
+    swapped_nibbles = ((m & 0xF) << 4) | (m >> 4)
+    d = oracle.decode(oracle.BF16, oracle.expand_sp24(vals, np.array([[swapped_nibbles]], np.uint8), 8)[0])
+    assert d.tolist() != exp
+    rev = vals.copy()
+    rev[0, 0::2], rev[0, 1::2] = vals[0, 1::2], vals[0, 0::2]
+    d = oracle.decode(oracle.BF16, oracle.expand_sp24(rev, np.array([[m]], np.uint8), 8)[0])
+    assert d.tolist() != exp
