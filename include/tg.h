@@ -2,8 +2,9 @@
  * tg.h -- C ABI of the tile GEMM library for AMD MI355X (gfx950).
  *
  * The library computes the tile-decomposed matrix multiply C = A.B that
- * TileLang and TileScale use as their canonical kernel, and its weight-only
- * int4 "Dequant-GEMM" variant.  Operation, per call:
+ * TileLang and TileScale use as their canonical kernel, its weight-only
+ * int4 "Dequant-GEMM" variant and a 2:4 structured-sparse variant.
+ * Operation, per call:
  *
  *     C[i][j] = alpha * sum over k of A[i][k] * B[k][j]      (fp32 accumulate)
  *
@@ -18,7 +19,7 @@
  * 生态互操作、性能、局限与路线图.
  *
  * Conventions shared by every entry point
- *  - Pointers A, B, C, qweight, scales, W are DEVICE pointers owned by the
+ *  - Pointers A, B, C, qweight, scales, W, Wv, Wm are DEVICE pointers owned by the
  *    caller.  The library never allocates, frees or retains them and keeps no
  *    state between calls (it is reentrant).
  *  - Matrices are row-major with a leading dimension in ELEMENTS:
@@ -122,6 +123,33 @@ tg_status tg_dequant_w4(int64_t N, int64_t K,
                         int32_t group_size, int32_t zero_point,
                         void *W, int64_t ldw,
                         void *stream);
+
+/* 2:4 structured-sparse GEMM: bf16 activations x 2:4-sparse bf16 weights ->
+ * fp32 accumulate -> C of c_dtype (TG_F32, TG_F16 or TG_BF16, RNE).
+ *     C[i][j] = sum over k of A[i][k] * W[j][k]
+ * W is N x K (the transpose_B form) with at most 2 nonzero entries in every
+ * aligned group of 4 consecutive k of a row, stored compressed:
+ *   Wv : bf16 [N][ldv], ldv >= K/2: the 2 kept values of group g of row n at
+ *        Wv[n*ldv + 2g] and Wv[n*ldv + 2g + 1], in position order
+ *   Wm : uint8 [N][ldm], ldm >= K/8: the 4-bit code of group g of row n is
+ *        (Wm[n*ldm + g/2] >> (4*(g%2))) & 0xF = i0 | (i1 << 2), the positions
+ *        k = 4g + i0 and 4g + i1 of the two kept values, i0 < i1 (a group
+ *        with fewer nonzeros keeps zeros in its unused slots)
+ * Source: the sparse GEMM T.gemm_sp in the TileLang timeline of "TileScale
+ * 与 TileLang比较"; the page gives no storage format, this one is a reading
+ * (the layout of the gfx950 sparse matrix instructions' index operand).  A
+ * code with i0 >= i1 is outside the format: it is not checked (device data),
+ * and each kept value then multiplies the activation at its coded position.
+ * Supported: K % 64 == 0 (else TG_ERR_NOT_SUPPORTED).  Alignment: A, Wv, C
+ * 16 bytes with lda*2, ldv*2 and ldc*element size multiples of 16; Wm 4
+ * bytes with ldm a multiple of 4; else TG_ERR_MISALIGNED.  Other conventions
+ * as above (Wv, Wm are device pointers). */
+tg_status tg_gemm_sp24_bf16(int64_t M, int64_t N, int64_t K,
+                            const void *A, int64_t lda,
+                            const void *Wv, int64_t ldv,
+                            const void *Wm, int64_t ldm,
+                            void *C, int64_t ldc, tg_dtype c_dtype,
+                            void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *tg_status_string(tg_status status);

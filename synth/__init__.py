@@ -15,6 +15,11 @@ measured kernels are meant for; the pages print no shapes, so these stand in):
   w4a16         fp16 A 256x8192 N(0,1); int4 weights U{0..15} packed 8 per int32
                 along K ([N][K/8]); fp16 scales U(0.005,0.02) per 128 K per
                 column ([N][K/128]); zero point 8; fp16 out
+  sp24_4096     bf16 M=N=K=4096, A N(0,1) row-major; 2:4 sparse weights N x K:
+                kept values N(0,1) rounded to bf16 ([N][K/2]), each group's
+                pair of kept positions uniform over the 6 pairs, stored as
+                4-bit codes i0 | i1<<2, two per byte, low nibble first
+                ([N][K/8]); bf16 out
 """
 from __future__ import annotations
 
@@ -29,7 +34,11 @@ SEEDS = {
     "bf16_skinny": (5, 6),
     "fp8_8192": (7, 8),
     "w4a16": (9, 10, 11),
+    "sp24_4096": (12, 13, 14),
 }
+
+# the 6 position pairs (i0 < i1) of a group of 4, as the 4-bit code i0 | i1 << 2
+SP24_CODES = (0x4, 0x8, 0xC, 0x9, 0xD, 0xE)
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -56,6 +65,15 @@ def random_words(shape, seed: int) -> torch.Tensor:
     """int32 words with uniformly random bits: every nibble is i.i.d. U{0..15}."""
     t = torch.randint(0, 1 << 16, tuple(shape) + (2,), dtype=torch.int32, generator=_gen(seed))
     return (t[..., 0] | (t[..., 1] << 16)).contiguous()
+
+
+def sparse24_codes(shape, seed: int) -> torch.Tensor:
+    """uint8 [rows][K/8] of 2:4 group codes: each group's pair of kept positions
+    uniform over the 6 pairs, two 4-bit codes per byte, low nibble first."""
+    rows, nbytes = shape
+    pick = torch.randint(0, 6, (rows, nbytes, 2), generator=_gen(seed))
+    codes = torch.tensor(SP24_CODES, dtype=torch.int32)[pick]
+    return (codes[..., 0] | (codes[..., 1] << 4)).to(torch.uint8).contiguous()
 
 
 def quantize_e4m3(x: torch.Tensor):
@@ -113,4 +131,11 @@ def workload(name: str, M: int | None = None, N: int | None = None, K: int | Non
         scales = uniform((N, (K + group - 1) // group), ss, 0.005, 0.02).to(torch.float16)
         return dict(name=name, A=A, qweight=qweight, scales=scales, M=M, N=N, K=K,
                     group_size=group, zero_point=8, out="f16", dtype="w4a16")
+    if name == "sp24_4096":
+        M, N, K = M or 4096, N or 4096, K or 4096
+        sa, sv, sm = SEEDS[name]
+        A = normal((M, K), sa).to(torch.bfloat16)
+        vals = normal((N, K // 2), sv).to(torch.bfloat16)
+        meta = sparse24_codes((N, K // 8), sm)
+        return dict(name=name, A=A, vals=vals, meta=meta, M=M, N=N, K=K, out="bf16", dtype="bf16")
     raise KeyError(name)

@@ -23,7 +23,7 @@ def tg():
 
 def test_header_declares_expected_entry_points():
     assert _declared() == sorted(["tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16",
-                                  "tg_dequant_w4", "tg_status_string", "tg_version"])
+                                  "tg_dequant_w4", "tg_gemm_sp24_bf16", "tg_status_string", "tg_version"])
 
 
 def test_library_exports_every_declared_symbol(tg):
@@ -104,6 +104,38 @@ def test_w4a16_validation(tg):
     assert lib.tg_dequant_w4(8, 128, A16, 16, A16, 1, 128, 8, A16 + 2, 128, None) == tg.TG_ERR_MISALIGNED
     assert lib.tg_dequant_w4(8, 100, A16, 16, A16, 1, 128, 8, A16, 128, None) == tg.TG_ERR_NOT_SUPPORTED
     assert lib.tg_dequant_w4(0, 128, None, 16, None, 1, 128, 8, None, 128, None) == tg.TG_OK
+
+
+def test_sp24_validation(tg):
+    lib = ctypes.CDLL(tg.LIB_PATH)
+    lib.tg_gemm_sp24_bf16.argtypes = [ctypes.c_int64] * 3 + [ctypes.c_void_p, ctypes.c_int64] * 4 + [ctypes.c_int,
+                                                                                                    ctypes.c_void_p]
+    P = 1 << 20  # a fake 1 MiB-aligned device address: validation never dereferences it
+
+    def call(M=64, N=64, K=128, A=P, lda=128, V=P, ldv=64, W=P, ldm=16, C=P, ldc=64, dt=2):
+        return lib.tg_gemm_sp24_bf16(M, N, K, A, lda, V, ldv, W, ldm, C, ldc, dt, None)
+
+    assert call(M=-1) == tg.TG_ERR_INVALID_VALUE
+    assert call(K=-64) == tg.TG_ERR_INVALID_VALUE
+    assert call(dt=7) == tg.TG_ERR_INVALID_VALUE
+    assert call(K=96) == tg.TG_ERR_NOT_SUPPORTED       # K not a multiple of 64
+    assert call(M=0) == tg.TG_OK and call(N=0) == tg.TG_OK
+    assert call(C=0) == tg.TG_ERR_INVALID_VALUE
+    assert call(ldc=63) == tg.TG_ERR_INVALID_VALUE
+    assert call(A=0) == tg.TG_ERR_INVALID_VALUE and call(V=0) == tg.TG_ERR_INVALID_VALUE
+    assert call(W=0) == tg.TG_ERR_INVALID_VALUE
+    assert call(lda=127) == tg.TG_ERR_INVALID_VALUE    # lda < K
+    assert call(ldv=63) == tg.TG_ERR_INVALID_VALUE     # ldv < K/2
+    assert call(ldm=15) == tg.TG_ERR_INVALID_VALUE     # ldm < K/8
+    assert call(A=P + 2) == tg.TG_ERR_MISALIGNED
+    assert call(V=P + 8) == tg.TG_ERR_MISALIGNED
+    assert call(lda=132) == tg.TG_ERR_MISALIGNED       # lda*2 not a multiple of 16
+    assert call(ldv=68) == tg.TG_ERR_MISALIGNED
+    assert call(W=P + 2) == tg.TG_ERR_MISALIGNED       # codes need 4-byte alignment
+    assert call(ldm=18) == tg.TG_ERR_MISALIGNED
+    assert call(C=P + 4) == tg.TG_ERR_MISALIGNED
+    assert call(ldc=66, dt=2) == tg.TG_ERR_MISALIGNED  # 66 bf16 = 132 bytes
+    assert call(lda=1 << 30) == tg.TG_ERR_NOT_SUPPORTED  # offsets past the buffer-resource range
 
 
 def test_product_and_oracle_share_no_code():

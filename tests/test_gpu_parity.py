@@ -453,3 +453,59 @@ def test_workload_w4a16_decode(tg, M):
     cref, S = oracle.w4a16(A, q, s, K)
     ok, r, idx = ochk.check(_f64(C), cref, S, K, "f16")
     assert ok, (r, idx)
+
+
+# ------------------------------------------------------------- 2:4 sparse
+
+def _sp_inputs(M, N, K, seed):
+    A = synth.normal((M, K), seed).to(torch.bfloat16)
+    vals = synth.normal((N, K // 2), seed + 1).to(torch.bfloat16)
+    meta = synth.sparse24_codes((N, K // 8), seed + 2)
+    return A, vals, meta
+
+
+def _run_sp(tg, A, vals, meta, out):
+    M, N = A.shape[0], vals.shape[0]
+    store = torch.full((M, (N + 7) // 8 * 8), float("nan"), dtype=ODT[out], device="cuda")
+    C = store[:, :N]
+    tg.tg_gemm_sp24_bf16(A.cuda(), vals.cuda(), meta.cuda(), C)
+    torch.cuda.synchronize()
+    return C
+
+
+# one tile and many, ragged M and N on both sides of the 256 tile, K of one
+# step (64) and several
+@pytest.mark.parametrize("shape", [(1, 1, 64), (7, 9, 64), (64, 64, 128), (256, 256, 256), (300, 260, 512),
+                                   (513, 200, 1024), (1000, 1100, 192)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+def test_sp24_small(tg, out, shape):
+    M, N, K = shape
+    A, v, m = _sp_inputs(M, N, K, seed=M + 2 * N + K)
+    C = _run_sp(tg, A, v, m, out)
+    cref, S = oracle.gemm_sp24(A, v, m, K)
+    ok, r, idx = ochk.check(_f64(C), cref, S, K, out)
+    assert ok, (r, idx)
+
+
+def test_sp24_one_hot_rows_read_the_weights(tg):
+    """A row that is one-hot at k gives C[., n] = W[n][k] exactly: every kept value
+    lands at its coded position and every other position contributes zero."""
+    N, K = 300, 256
+    _, v, m = _sp_inputs(1, N, K, seed=61)
+    ks = list(range(0, K, 3)) + [K - 1]
+    A = torch.zeros((len(ks), K), dtype=torch.bfloat16)
+    for i, k in enumerate(ks):
+        A[i, k] = 1.0
+    C = _run_sp(tg, A, v, m, "f32")
+    W = oracle.decode(oracle.BF16, oracle.expand_sp24(v, m, K))
+    assert np.array_equal(_f64(C), W[:, ks].T)
+
+
+def test_workload_sp24_4096(tg):
+    w = synth.workload("sp24_4096")
+    A, v, m, K = w["A"], w["vals"], w["meta"], w["K"]
+    C = _run_sp(tg, A, v, m, "bf16")
+    rows = np.r_[0:8, 2040:2048, 4088:4096]
+    cref, S = oracle.gemm_sp24(A[rows], v, m, K)
+    ok, r, idx = ochk.check(_f64(C[rows]), cref, S, K, "bf16")
+    assert ok, (r, idx)

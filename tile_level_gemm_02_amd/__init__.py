@@ -35,7 +35,7 @@ TG_F32, TG_F16, TG_BF16 = 0, 1, 2
 TG_ROW_MAJOR, TG_COL_MAJOR = 0, 1
 
 EXPORTS = ("tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16", "tg_dequant_w4",
-           "tg_status_string", "tg_version")
+           "tg_gemm_sp24_bf16", "tg_status_string", "tg_version")
 
 
 class TGError(RuntimeError):
@@ -57,6 +57,7 @@ def _load() -> ctypes.CDLL:
     lib.tg_gemm_fp8.argtypes = [i64, i64, i64, vp, i64, vp, i64, ci, f32, f32, vp, i64, ci, vp]
     lib.tg_gemm_w4a16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, i32, vp, i64, vp]
     lib.tg_dequant_w4.argtypes = [i64, i64, vp, i64, vp, i64, i32, i32, vp, i64, vp]
+    lib.tg_gemm_sp24_bf16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, vp]
     for name in ("tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16", "tg_dequant_w4"):
         getattr(lib, name).restype = ci
     lib.tg_status_string.argtypes = [ci]
@@ -137,6 +138,23 @@ def tg_gemm_bf16(A, B, C, b_layout: str = "row", stream=None) -> None:
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise ValueError("tg_gemm_bf16 takes bfloat16 A and B")
     _ok("tg_gemm_bf16", lib.tg_gemm_bf16(*_dense("tg_gemm_bf16", A, B, C, b_layout, stream)))
+
+
+def tg_gemm_sp24_bf16(A, Wv, Wm, C, stream=None) -> None:
+    """C = A . W^T with bf16 A and 2:4-sparse bf16 weights W given compressed:
+    kept values Wv bf16 [N][K/2], group codes Wm uint8 [N][K/8]; see include/tg.h."""
+    if A.dtype != torch.bfloat16 or Wv.dtype != torch.bfloat16 or Wm.dtype != torch.uint8:
+        raise ValueError("tg_gemm_sp24_bf16 takes bfloat16 A and Wv and uint8 Wm")
+    M, K, lda, pa = _mat(A, "A")
+    N, Kv, ldv, pv = _mat(Wv, "Wv")
+    Nm, Km, ldm, pm = _mat(Wm, "Wm")
+    Mc, Nc, ldc, pc = _mat(C, "C")
+    if Kv != K // 2 or Km != K // 8 or Nm != N or (Mc, Nc) != (M, N):
+        raise ValueError("inconsistent sparse GEMM shapes")
+    if C.dtype not in _CDTYPE:
+        raise ValueError(f"unsupported C dtype {C.dtype}")
+    _ok("tg_gemm_sp24_bf16", lib.tg_gemm_sp24_bf16(M, N, K, pa, lda, pv, ldv, pm, ldm, pc, ldc,
+                                                   _CDTYPE[C.dtype], _stream(stream)))
 
 
 def tg_gemm_fp8(A, B, C, scale_a: float, scale_b: float, b_layout: str = "col", stream=None) -> None:

@@ -1,0 +1,288 @@
+// 2:4 structured-sparse GEMM: C = A . W^T with A bf16 M x K (row-major) and
+// W bf16 N x K holding at most 2 nonzeros in every aligned group of 4
+// consecutive k, stored compressed (the kept values, [N][K/2], and a 4-bit
+// code i0 | i1 << 2 of their positions per group, two per byte, [N][K/8]).
+// The operation is the sparse GEMM T.gemm_sp in the TileLang timeline of
+// "TileScale 与 TileLang比较"; the tile dataflow is the page's single-GPU GEMM
+// skeleton (section 核心抽象与编程模型对比), as in the dense NT kernel.
+//
+// gfx950's sparse matrix instruction v_smfmac_f32_32x32x32_bf16 takes the
+// compressed operand directly: for a 32 x 32 (dense) k block, lane l supplies
+// row l%32 of the sparse operand as 8 kept values -- the groups 4h .. 4h+3
+// of the block, h = l/32 -- and 16 bits of index, 2 per value, which is this
+// format's codes for those 4 groups byte for byte.  The dense operand's lane l
+// holds column l%32 at k = 8h .. 8h+7 and 16+8h .. 16+8h+7.  The weights are
+// the sparse operand, so the output block is transposed exactly as in the
+// NT kernel (lane l holds 4-column runs of output row l%32).
+//
+// Tile 256 x 256, 8 waves (2 x 4, each 128 x 64), a K step of 64: per step
+// 32 KB of A rows (128 B per row, 16-byte chunks XOR-swizzled by row pair),
+// 16 KB of kept values (64 B per row, chunks swizzled by row quad) and 2 KB
+// of codes (8 B per row), all copied straight into LDS.  A ring of 3 such
+// stages with one barrier per step: the copies of step k+3 are issued, spread
+// between the MFMAs, right after the barrier that frees step k's stage.
+#pragma once
+
+#include "tg_gemm_nt.hpp"
+
+namespace tg {
+
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+
+struct SpArgs {
+    int64_t M, N, K;
+    const uint8_t* A;
+    int64_t lda;  // elements
+    const uint8_t* Wv;
+    int64_t ldv;  // elements
+    const uint8_t* Wm;
+    int64_t ldm;  // bytes
+    void* C;
+    int64_t ldc;  // elements
+    uint32_t group_m;
+};
+
+// One wave instruction: 64 lanes x 4 bytes from global memory straight into
+// the 256 bytes of LDS at address `dst` (lane i lands at dst + 4*i).
+__device__ __forceinline__ void load_lds_256_at(i32x4_t r, uint32_t dst, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(soff), "{m0}"(dst)
+                 : "memory");
+}
+
+constexpr int kSpThreads = 512;
+
+template <int O>
+__global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
+{
+    constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NW = WM * WN;
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 4 x 2 blocks of 32 x 32 per wave
+    constexpr int KE = 64;                              // dense k per step
+    constexpr int AB = BM * 128, VB = BN * 64, MB = BN * 8;
+    constexpr int STAGE = AB + VB + MB;
+    constexpr int NS = 3;
+    constexpr int PER = 4 + 2 + 1;  // copy instructions per wave per step: A rows, values, codes
+    static_assert(NS * STAGE <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
+    const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
+    uint32_t tmi, tni;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, p.group_m, tmi, tni);
+    const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
+    const uint32_t ldab = (uint32_t)(p.lda * 2), ldvb = (uint32_t)(p.ldv * 2), ldmb = (uint32_t)p.ldm;
+    const int32_t rows_a = (int32_t)(M - m0 < BM ? M - m0 : BM);
+    const int32_t rows_w = (int32_t)(N - n0 < BN ? N - n0 : BN);
+    const i32x4_t ra = make_rsrc(p.A + m0 * (int64_t)ldab);
+    const i32x4_t rv = make_rsrc(p.Wv + n0 * (int64_t)ldvb);
+    const i32x4_t rm = make_rsrc(p.Wm + n0 * (int64_t)ldmb);
+    const int64_t KT = K / KE;  // K is a multiple of KE
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+
+    // ---- copy lanes.  A: instruction j covers rows 32w + 8j .. +7 (lane/8),
+    // physical chunk lane%8 holding logical chunk (lane%8) ^ ((row/2)%8): one
+    // value for even j, one for odd j.  Values: instruction j covers rows
+    // 32w + 16j .. +15 (lane/4), physical chunk lane%4 holding logical chunk
+    // (lane%4) ^ ((row/4)%4).  Codes: rows 32w .. +31 (lane/2), dword lane%2.
+    const uint32_t arow = wave * 32u + lane / 8u;
+    const uint32_t ach0 = (lane % 8u) ^ ((lane / 16u) % 8u);
+    const uint32_t ach1 = (lane % 8u) ^ ((4u + lane / 16u) % 8u);
+    const uint32_t vrow = wave * 32u + lane / 4u;
+    const uint32_t vch = (lane % 4u) ^ ((lane / 16u) % 4u);
+    const uint32_t mrow = wave * 32u + lane / 2u;
+    const uint32_t va0 = arow * ldab + ach0 * 16u, va1 = arow * ldab + ach1 * 16u;
+    const uint32_t vv = vrow * ldvb + vch * 16u;
+    const uint32_t vm = mrow * ldmb + (lane % 2u) * 4u;
+
+    // copy instruction q (0 .. PER-1) of step kt into stage slot `st`
+    auto copy = [&](auto edge, int64_t kt, uint32_t st, int q) __attribute__((always_inline)) {
+        const uint32_t past = kt < KT ? 0u : kOutOfRange;
+        const uint32_t base = lds0 + st * STAGE;
+        if (q < 4) {
+            uint32_t v = ((q & 1) ? va1 : va0) | past;
+            if constexpr (decltype(edge)::value)
+                v |= (int32_t)(arow + 8u * q) < rows_a ? 0u : kOutOfRange;
+            load_lds_1k_at(ra, base + wave * 4096u + q * 1024u, v, (uint32_t)kt * 128u + (uint32_t)(8 * q) * ldab);
+        } else if (q < 6) {
+            const int j = q - 4;
+            uint32_t v = vv | past;
+            if constexpr (decltype(edge)::value)
+                v |= (int32_t)(vrow + 16u * j) < rows_w ? 0u : kOutOfRange;
+            load_lds_1k_at(rv, base + AB + wave * 2048u + j * 1024u, v,
+                           (uint32_t)kt * 64u + (uint32_t)(16 * j) * ldvb);
+        } else {
+            uint32_t v = vm | past;
+            if constexpr (decltype(edge)::value)
+                v |= (int32_t)mrow < rows_w ? 0u : kOutOfRange;
+            load_lds_256_at(rm, base + AB + VB + wave * 256u, v, (uint32_t)kt * 8u);
+        }
+    };
+
+    // ---- fragments.  Every row a lane reads has the same swizzle.
+    const uint32_t wm = wave / WN, wn = wave % WN;
+    const uint32_t lrow = lane & 31u, h = lane >> 5;
+    const uint32_t swa = (lrow / 2u) % 8u, swv = (lrow / 4u) % 4u;
+    const uint32_t a_row0 = (wm * (BM / WM) + lrow) * 128u;
+    const uint32_t w_row0 = wn * (BN / WN) + lrow;
+    u32x4 fx[2][TM][2], fw[2][TN];
+    uint32_t fi[2][TN];
+    auto read_frags = [&](int64_t kt, int s, int slot) __attribute__((always_inline)) {
+        const uint8_t* st = lds + (uint32_t)(kt % NS) * STAGE;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const uint32_t r = a_row0 + i * 32 * 128;
+            fx[slot][i][0] = lds128(st, r + ((((uint32_t)(4 * s) + h) ^ swa) << 4));
+            fx[slot][i][1] = lds128(st, r + ((((uint32_t)(4 * s + 2) + h) ^ swa) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const uint32_t r = w_row0 + j * 32;
+            fw[slot][j] = lds128(st, AB + r * 64u + ((((uint32_t)(2 * s) + h) ^ swv) << 4));
+            fi[slot][j] = *(const uint16_t*)(st + AB + VB + r * 8u + 4u * s + 2u * h);
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = f32x16{};
+    // one sub-step (32 dense k): the TM*TN sparse MFMAs of fragment slot
+    // `slot`, with NQ copy instructions spread between them
+    auto mma = [&](int slot, auto cp, auto nq) __attribute__((always_inline)) {
+        constexpr int NQ = decltype(nq)::value, NT = TM * TN;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int i = t / TN, j = t % TN;
+            const u32x4 x0 = fx[slot][i][0], x1 = fx[slot][i][1];
+            const i32x8 xb = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                              (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+            acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(bit_cast<bf16x8>(fw[slot][j]), bit_cast<bf16x16>(xb),
+                                                                 acc[i][j], (int)fi[slot][j], 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                if (q * NT / NQ == t)
+                    cp(q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto nothing = [](int) {};
+
+    // One K step (2 sub-steps).  Entering, the fragments of its sub-step 0
+    // are in slot 0.  The barrier publishes step kt+1 (step kt+2 may still be
+    // in flight) and frees step kt's stage, into which step kt+3 is copied
+    // during the second sub-step while step kt+1's first fragments are read.
+    auto step = [&](auto edge, int64_t kt) __attribute__((always_inline)) {
+        read_frags(kt, 1, 1);
+        mma(0, nothing, std::integral_constant<int, 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        wait_copies<PER>();
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(kt + 1, 0, 0);  // (stale, unused, after the last step)
+        const uint32_t slot = (uint32_t)(kt % NS);
+        mma(1, [&](int q) __attribute__((always_inline)) { copy(edge, kt + NS, slot, q); },
+            std::integral_constant<int, PER>{});
+    };
+    auto run = [&](auto edge) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+            for (int q = 0; q < PER; ++q)
+                copy(edge, st, (uint32_t)st, q);
+        wait_copies<(NS - 1) * PER>();  // step 0 landed
+        __syncthreads();
+        read_frags(0, 0, 0);
+        for (int64_t kt = 0; kt < KT; ++kt)
+            step(edge, kt);
+        wait_copies<0>();  // copies past the last step (zeros) land before LDS is reused
+    };
+    if (KT > 0) {
+        if (rows_a == BM && rows_w == BN)
+            run(std::false_type{});
+        else
+            run(std::true_type{});
+    }
+    mfma_drain();
+
+    // ---- epilogue (the NT kernel's layout: value v of lane l of acc[i][j] is
+    // C[m = i*32 + l%32][n = j*32 + 8*(v/4) + 4*(l/32) + v%4] of the wave's sub-tile)
+    constexpr int WR = BM / WM, WC = BN / WN;
+    const int64_t wrow0 = m0 + wm * WR, wcol0 = n0 + wn * WC;
+    if constexpr (O == O_F32) {
+        float* C = (float*)p.C;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t row = wrow0 + i * 32 + lrow;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t col = wcol0 + j * 32 + 8 * g + 4 * h;
+                    const f32x4 q = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    if (row < M) {
+                        if (col + 4 <= N) {
+                            *(f32x4*)(C + row * p.ldc + col) = q;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (col + e < N)
+                                    C[row * p.ldc + col + e] = q[e];
+                        }
+                    }
+                }
+            }
+        }
+    } else {
+        // 16-bit output: each wave stages its sub-tile in its own LDS region
+        // (row-major, 16-byte chunks XOR-swizzled by row), then writes whole rows
+        constexpr int OB = WC * 2, NCH = OB / 16, WBYTES = WR * OB;
+        static_assert(NW * WBYTES <= NS * STAGE, "epilogue staging must fit the stages");
+        __syncthreads();  // every wave is done reading the stages
+        uint8_t* ep = lds + wave * WBYTES;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const uint32_t r = i * 32 + lrow;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t c = (uint32_t)(4 * j + g);
+                    const uint32_t lo = (uint32_t)convert_out<O>(acc[i][j][4 * g]) |
+                                        ((uint32_t)convert_out<O>(acc[i][j][4 * g + 1]) << 16);
+                    const uint32_t hi = (uint32_t)convert_out<O>(acc[i][j][4 * g + 2]) |
+                                        ((uint32_t)convert_out<O>(acc[i][j][4 * g + 3]) << 16);
+                    *(u32x2*)(ep + r * OB + ((c ^ (r % NCH)) << 4) + h * 8) = u32x2{lo, hi};
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes done
+        uint16_t* C = (uint16_t*)p.C;
+#pragma unroll
+        for (int t = 0; t < WR * NCH / 64; ++t) {
+            const uint32_t idx = t * 64 + lane;
+            const uint32_t r = idx / NCH, c = idx % NCH;
+            const u32x4 q = lds128(ep, r * OB + ((c ^ (r % NCH)) << 4));
+            const int64_t row = wrow0 + r, col = wcol0 + c * 8;
+            if (row < M) {
+                if (col + 8 <= N) {
+                    *(u32x4*)(C + row * p.ldc + col) = q;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (col + e < N)
+                            C[row * p.ldc + col + e] = (uint16_t)(q[e >> 1] >> ((e & 1) * 16));
+                }
+            }
+        }
+    }
+}
+
+}  // namespace tg

@@ -1,0 +1,62 @@
+// tg_gemm_sp24_bf16: 2:4 structured-sparse GEMM (contract in include/tg.h).
+#include "tg_gemm_sp.hpp"
+#include "tg_host.hpp"
+
+namespace {
+
+// gemm_sp24 addresses each operand through a buffer resource of kNumRecords
+// bytes based at its tile's first row: every offset it forms must stay below
+// that bound.
+bool sp24_offsets_fit(int64_t K, int64_t lda, int64_t ldv, int64_t ldm)
+{
+    const int64_t lim = (int64_t)tg::kNumRecords;
+    return 256 * lda * 2 + K * 2 < lim && 256 * ldv * 2 + K < lim && 256 * ldm + K / 8 < lim;
+}
+
+}  // namespace
+
+extern "C" tg_status tg_gemm_sp24_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                       const void* Wv, int64_t ldv, const void* Wm, int64_t ldm,
+                                       void* C, int64_t ldc, tg_dtype c_dtype, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return TG_ERR_INVALID_VALUE;
+    if (c_dtype != TG_F32 && c_dtype != TG_F16 && c_dtype != TG_BF16)
+        return TG_ERR_INVALID_VALUE;
+    if (K % 64 != 0)
+        return TG_ERR_NOT_SUPPORTED;
+    if (M == 0 || N == 0)
+        return TG_OK;
+    if (C == nullptr || ldc < N)
+        return TG_ERR_INVALID_VALUE;
+    if (K > 0) {
+        if (A == nullptr || Wv == nullptr || Wm == nullptr)
+            return TG_ERR_INVALID_VALUE;
+        if (lda < K || ldv < K / 2 || ldm < K / 8)
+            return TG_ERR_INVALID_VALUE;
+        if (!tg::aligned16(A) || !tg::aligned16(Wv) || ((lda * 2) & 15) || ((ldv * 2) & 15) ||
+            ((uintptr_t)Wm & 3u) || (ldm & 3))
+            return TG_ERR_MISALIGNED;
+        if (!sp24_offsets_fit(K, lda, ldv, ldm))
+            return TG_ERR_NOT_SUPPORTED;
+    }
+    if (!tg::aligned16(C) || ((ldc * tg::out_bytes(c_dtype)) & 15))
+        return TG_ERR_MISALIGNED;
+    tg::SpArgs a{M, N, K, (const uint8_t*)A, lda, (const uint8_t*)Wv, ldv, (const uint8_t*)Wm, ldm, C, ldc, 4};
+    const int64_t tiles = tg::n_tiles<256, 256>(M, N);
+    if (tiles > 0x7FFFFFFF)
+        return TG_ERR_NOT_SUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    switch (c_dtype) {
+    case TG_F32:
+        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_F32>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
+        break;
+    case TG_F16:
+        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_F16>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
+        break;
+    default:
+        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_BF16>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
+        break;
+    }
+    return tg::launched();
+}
