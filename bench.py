@@ -14,8 +14,8 @@ achieved TFLOP/s against the dense bf16 MFMA peak, from HIP events around
 each launch inside the timed region), `cpu_baseline` (the CPU oracle timed
 on a bounded sample of the same workload) and `secondary` (the skinny M=16
 GEMM's GB/s against the HBM peak, the same GEMM on an 8-way column shard
-(N=1024), the fp8 and w4a16 workloads, and the w4a16 weights at decode batch
-sizes M=16 and M=1), each
+(N=1024), the fp8 and w4a16 workloads, the w4a16 weights at decode batch
+sizes M=16 and M=1, and the 2:4 sparse GEMM at 4096^3), each
 secondary timed launch by launch with the 256 MB Infinity Cache flushed
 (by a 512 MiB read) before every launch.
 """
@@ -144,6 +144,22 @@ def setup_skinny_shard():
     return w, fn, flops, bytes_
 
 
+def setup_sp24():
+    """2:4 sparse weights at 4096^3: bf16 A, compressed bf16 W (values + codes), bf16 out."""
+    import torch
+    import synth
+    import tile_level_gemm_02_amd as tg
+
+    w = synth.workload("sp24_4096")
+    A, v, m = w["A"].cuda(), w["vals"].cuda(), w["meta"].cuda()
+    C = torch.empty((w["M"], w["N"]), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: tg.tg_gemm_sp24_bf16(A, v, m, C)
+    M, N, K = w["M"], w["N"], w["K"]
+    flops = 2.0 * M * N * K  # dense-equivalent
+    bytes_ = 2 * M * K + N * K + N * K // 8 + 2 * M * N
+    return w, fn, flops, bytes_
+
+
 def setup_fp8():
     import torch
     import synth
@@ -213,7 +229,7 @@ def main():
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (to scale HBM byte counters)")
     ap.add_argument("--only", choices=["bf16_4096", "bf16_skinny", "bf16_skinny_n1024", "fp8_8192", "w4a16", "w4a16_m16",
-                                       "w4a16_m1"],
+                                       "w4a16_m1", "sp24_4096"],
                     default=None,
                     help="only run this workload's launches (for counter collection), no JSON line")
     args = ap.parse_args()
@@ -243,7 +259,7 @@ def main():
     if args.only:
         setup = {"bf16_4096": setup_bf16_4096, "bf16_skinny": setup_skinny, "bf16_skinny_n1024": setup_skinny_shard,
                  "fp8_8192": setup_fp8,
-                 "w4a16": setup_w4a16, "w4a16_m16": lambda: setup_w4a16(16),
+                 "w4a16": setup_w4a16, "w4a16_m16": lambda: setup_w4a16(16), "sp24_4096": setup_sp24,
                  "w4a16_m1": lambda: setup_w4a16(1)}[args.only]
         _, fn, _, _ = setup()
         for _ in range(args.warmup):
@@ -305,7 +321,8 @@ def main():
                                       ("fp8_8192", setup_fp8, "fp8"),
                                       ("w4a16", setup_w4a16, "both"),
                                       ("w4a16_m16", lambda: setup_w4a16(16), "hbm"),
-                                      ("w4a16_m1", lambda: setup_w4a16(1), "hbm")):
+                                      ("w4a16_m1", lambda: setup_w4a16(1), "hbm"),
+                                      ("sp24_4096", setup_sp24, "sp")):
             w2, fn2, fl2, by2 = setup()
             for _ in range(3):
                 fn2()
@@ -317,6 +334,8 @@ def main():
                    "algorithmic_bytes": by2, "flop": fl2}
             if peak_key == "fp8":
                 rec["mfma_frac"] = round(fl2 / t / 1e12 / PEAK_FP8_TFLOPS, 4)
+            elif peak_key == "sp":  # dense-equivalent FLOP against the 2:4 sparse rate (twice dense bf16)
+                rec["mfma_frac"] = round(fl2 / t / 1e12 / (2 * PEAK_BF16_TFLOPS), 4)
             else:
                 rec["mfma_frac"] = round(fl2 / t / 1e12 / PEAK_BF16_TFLOPS, 4)
             sec[name] = rec

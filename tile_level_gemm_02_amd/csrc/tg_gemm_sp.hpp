@@ -99,10 +99,10 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
     const uint32_t vv = vrow * ldvb + vch * 16u;
     const uint32_t vm = mrow * ldmb + (lane % 2u) * 4u;
 
-    // copy instruction q (0 .. PER-1) of step kt into stage slot `st`
-    auto copy = [&](auto edge, int64_t kt, uint32_t st, int q) __attribute__((always_inline)) {
+    // copy instruction q (0 .. PER-1) of step kt into the stage at byte offset `so`
+    auto copy = [&](auto edge, int64_t kt, uint32_t so, int q) __attribute__((always_inline)) {
         const uint32_t past = kt < KT ? 0u : kOutOfRange;
-        const uint32_t base = lds0 + st * STAGE;
+        const uint32_t base = lds0 + so;
         if (q < 4) {
             uint32_t v = ((q & 1) ? va1 : va0) | past;
             if constexpr (decltype(edge)::value)
@@ -131,19 +131,21 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
     const uint32_t w_row0 = wn * (BN / WN) + lrow;
     u32x4 fx[2][TM][2], fw[2][TN];
     uint32_t fi[2][TN];
-    auto read_frags = [&](int64_t kt, int s, int slot) __attribute__((always_inline)) {
-        const uint8_t* st = lds + (uint32_t)(kt % NS) * STAGE;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const uint32_t r = a_row0 + i * 32 * 128;
-            fx[slot][i][0] = lds128(st, r + ((((uint32_t)(4 * s) + h) ^ swa) << 4));
-            fx[slot][i][1] = lds128(st, r + ((((uint32_t)(4 * s + 2) + h) ^ swa) << 4));
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const uint32_t r = w_row0 + j * 32;
-            fw[slot][j] = lds128(st, AB + r * 64u + ((((uint32_t)(2 * s) + h) ^ swv) << 4));
-            fi[slot][j] = *(const uint16_t*)(st + AB + VB + r * 8u + 4u * s + 2u * h);
+    // fragment read r (0 .. TM+TN-1) of sub-step s from the stage at byte
+    // offset `so` into slot `slot`, numbered in the order the MFMAs consume
+    // them: A block 0, every W block (values and codes), A blocks 1 .. TM-1
+    auto read_frag = [&](uint32_t so, int s, int slot, int r) __attribute__((always_inline)) {
+        const uint8_t* st = lds + so;
+        if (r >= 1 && r <= TN) {
+            const int j = r - 1;
+            const uint32_t row = w_row0 + j * 32;
+            fw[slot][j] = lds128(st, AB + row * 64u + ((((uint32_t)(2 * s) + h) ^ swv) << 4));
+            fi[slot][j] = *(const uint16_t*)(st + AB + VB + row * 8u + 4u * s + 2u * h);
+        } else {
+            const int i = r == 0 ? 0 : r - TN;
+            const uint32_t row = a_row0 + i * 32 * 128;
+            fx[slot][i][0] = lds128(st, row + ((((uint32_t)(4 * s) + h) ^ swa) << 4));
+            fx[slot][i][1] = lds128(st, row + ((((uint32_t)(4 * s + 2) + h) ^ swa) << 4));
         }
     };
 
@@ -153,10 +155,13 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             acc[i][j] = f32x16{};
-    // one sub-step (32 dense k): the TM*TN sparse MFMAs of fragment slot
-    // `slot`, with NQ copy instructions spread between them
-    auto mma = [&](int slot, auto cp, auto nq) __attribute__((always_inline)) {
-        constexpr int NQ = decltype(nq)::value, NT = TM * TN;
+    // One sub-step (32 dense k): the TM*TN sparse MFMAs of fragment slot
+    // `slot`.  The fragment reads of the next sub-step and NQ copy
+    // instructions are spread evenly over them, each pinned in place, so the
+    // in-order issue never waits on a burst.
+    constexpr int NT = TM * TN, NR = TM + TN;
+    auto substep = [&](int slot, auto rd, auto cp, auto nq) __attribute__((always_inline)) {
+        constexpr int NQ = decltype(nq)::value;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int i = t / TN, j = t % TN;
@@ -167,6 +172,10 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
                                                                  acc[i][j], (int)fi[slot][j], 0, 0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
+            for (int r = 0; r < NR; ++r)
+                if (r * NT / NR == t)
+                    rd(r);
+#pragma unroll
             for (int q = 0; q < NQ; ++q)
                 if (q * NT / NQ == t)
                     cp(q);
@@ -175,33 +184,40 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
     };
     auto nothing = [](int) {};
 
-    // One K step (2 sub-steps).  Entering, the fragments of its sub-step 0
-    // are in slot 0.  The barrier publishes step kt+1 (step kt+2 may still be
-    // in flight) and frees step kt's stage, into which step kt+3 is copied
-    // during the second sub-step while step kt+1's first fragments are read.
-    auto step = [&](auto edge, int64_t kt) __attribute__((always_inline)) {
-        read_frags(kt, 1, 1);
-        mma(0, nothing, std::integral_constant<int, 0>{});
+    // One K step (2 sub-steps) on the stage at byte offset `cur` (step kt+1's
+    // at `nxt`).  Entering, the fragments of its sub-step 0 are in slot 0.
+    // The barrier publishes step kt+1 (step kt+2 may still be in flight) and
+    // frees step kt's stage, into which step kt+3 is copied during the second
+    // sub-step while step kt+1's first fragments are read.
+    auto step = [&](auto edge, int64_t kt, uint32_t cur, uint32_t nxt) __attribute__((always_inline)) {
+        substep(0, [&](int r) __attribute__((always_inline)) { read_frag(cur, 1, 1, r); }, nothing,
+                std::integral_constant<int, 0>{});
         __builtin_amdgcn_sched_barrier(0);
         wait_copies<PER>();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(kt + 1, 0, 0);  // (stale, unused, after the last step)
-        const uint32_t slot = (uint32_t)(kt % NS);
-        mma(1, [&](int q) __attribute__((always_inline)) { copy(edge, kt + NS, slot, q); },
-            std::integral_constant<int, PER>{});
+        // (the reads of step kt+1 after the last step are stale and unused)
+        substep(1, [&](int r) __attribute__((always_inline)) { read_frag(nxt, 0, 0, r); },
+                [&](int q) __attribute__((always_inline)) { copy(edge, kt + NS, cur, q); },
+                std::integral_constant<int, PER>{});
     };
     auto run = [&](auto edge) __attribute__((always_inline)) {
 #pragma unroll
         for (int st = 0; st < NS; ++st)
 #pragma unroll
             for (int q = 0; q < PER; ++q)
-                copy(edge, st, (uint32_t)st, q);
+                copy(edge, st, (uint32_t)(st * STAGE), q);
         wait_copies<(NS - 1) * PER>();  // step 0 landed
         __syncthreads();
-        read_frags(0, 0, 0);
-        for (int64_t kt = 0; kt < KT; ++kt)
-            step(edge, kt);
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            read_frag(0, 0, 0, r);
+        uint32_t cur = 0;  // byte offset of step kt's stage
+        for (int64_t kt = 0; kt < KT; ++kt) {
+            const uint32_t nxt = cur == (NS - 1) * STAGE ? 0u : cur + STAGE;
+            step(edge, kt, cur, nxt);
+            cur = nxt;
+        }
         wait_copies<0>();  // copies past the last step (zeros) land before LDS is reused
     };
     if (KT > 0) {
