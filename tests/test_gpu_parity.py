@@ -122,6 +122,23 @@ def test_skinny_ragged(tg, dt, M):
     _check(C, A, B, dt, "col", "f32")
 
 
+# The skinny kernel with 16-bit outputs and padded leading dimensions: K
+# shorter than one block per wave, K with only a partial block, whole blocks
+# only, and whole blocks plus a partial 16-byte chunk.
+@pytest.mark.parametrize("K", [16, 40, 4096, 4101])
+@pytest.mark.parametrize("M", [1, 9, 16])
+@pytest.mark.parametrize("out", ["f16", "bf16"])
+def test_skinny_outputs_strided(tg, out, M, K):
+    N = 1000
+    dt = "bf16" if out == "f16" else "f16"
+    A, B, _, _ = _inputs(dt, M, N, K, "col", seed=M * 7 + K)
+    pad = (-K) % 8 + 16
+    store = torch.full((M, N + 24), float("nan"), dtype=ODT[out], device="cuda")
+    C = _run_dense(tg, dt, A, B, "col", out, pad=pad, C=store[:, :N])
+    _check(C, A, B, dt, "col", out)
+    assert torch.isnan(store[:, N:]).all()
+
+
 # Narrow N with fp32 output (a column shard of the skinny workload): the
 # skinny kernel also splits K over workgroups and adds their partial tiles
 # into a zeroed C with fp32 atomics.  Ragged N and K, a split count that does

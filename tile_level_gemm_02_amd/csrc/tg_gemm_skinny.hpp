@@ -1,0 +1,200 @@
+// The GEMM for M <= 16 rows against a K-contiguous B (decode-shaped products:
+// a few activation rows against a weight stored N x K).  Streaming B from
+// HBM is the whole cost.  The waves of a workgroup split K and reduce their
+// partial tiles through LDS -- the intra-block split-K of the TileScale
+// README's GEMM example (section "Example of GEMM"), where warpgroups split
+// K and all-reduce on chip.
+//
+// Each workgroup owns 16 columns (B rows).  Each wave streams its K range
+// through a private LDS ring of RING slots with direct-to-LDS copies; a slot
+// holds one stage of 64 k: 128 bytes of each of the 16 B rows and of the A
+// rows.  One copy instruction fetches 8 rows x 128 bytes -- whole cache lines
+// -- which the memory system streams faster than the 16 rows x 64 bytes a
+// lane-per-operand register load would fetch.  Chunks are XOR-swizzled by
+// row so the fragment reads are free of bank conflicts.  A wave waits only
+// for its own copies (no barrier in the loop); with RING = 2 the copies of
+// stage s+1 are in flight while stage s is multiplied, which measured faster
+// than deeper rings (more requests in flight stream no faster).
+//
+// MFMA: 16x16x32 with the operands swapped (B rows in the first operand):
+// lane l supplies 8 k of B column l%16 and of A row l%16 (rows past M read
+// as zeros), lane quarter h = l/16 takes k = 8h .. 8h+7 of each 32.  The
+// result lane l, value v is row l%16, column 4*(l/16) + v.
+//
+// A K tail (K % 64) is multiplied after the ring by one wave, from global
+// memory with element masks.
+#pragma once
+
+#include "tg_gemm_nt.hpp"
+
+namespace tg {
+
+constexpr int kSkCols = 16;   // columns (B rows) per workgroup
+constexpr int kSkKE = 64;     // k per stage
+constexpr int kSkRow = 128;   // bytes per staged row (16-bit elements)
+
+// Slot bytes: the 16 B rows, then 8*AI A rows (AI copy instructions).
+template <int AI> struct SkinnySlot {
+    static constexpr int BYTES = (kSkCols + 8 * AI) * kSkRow;
+};
+
+// physical 16-byte chunk of logical chunk c of staged row r: two rows share
+// a 256-byte line of the 64 banks, so 16 rows at one logical chunk land in 16
+// distinct bank groups
+__device__ __forceinline__ uint32_t sk_swz(uint32_t r, uint32_t c)
+{
+    return c ^ ((r >> 1) & 7u);
+}
+
+// SPLIT: the K stages are also split over gridDim.y workgroups per column
+// block (for narrow N, where N / 16 workgroups leave CUs idle); each adds
+// its partial tile into the fp32 output, which the host has zeroed (fp32
+// atomic adds, so the summation order over the split is not fixed).
+template <int E, int O, int WAVES, int AI, int RING, bool SPLIT = false>
+__global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
+{
+    typedef typename OutInfo<O>::T OutT;
+    static_assert(E == E_F16 || E == E_BF16, "16-bit inputs");
+    static_assert(!SPLIT || O == O_F32, "partial tiles are added in fp32");
+    constexpr int SLOT = SkinnySlot<AI>::BYTES;
+    constexpr int PER = 2 + AI;  // copy instructions per stage
+    constexpr int ZERO = WAVES * RING * SLOT;  // 16 zero bytes: A rows past 8*AI
+    static_assert(AI >= 1 && AI <= 2 && RING >= 2 && (RING - 1) * PER <= 63, "copy ring");
+    static_assert(ZERO + 16 <= 160 * 1024 && WAVES * 4 * 64 * 4 <= ZERO, "LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[ZERO + 16];
+
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t n0 = (int64_t)blockIdx.x * kSkCols;
+    const int64_t KS = K / kSkKE;  // whole stages
+    // this workgroup's stages [z0, z1), split over its waves in contiguous ranges
+    const int64_t z0 = SPLIT ? KS * blockIdx.y / gridDim.y : 0;
+    const int64_t z1 = SPLIT ? KS * (blockIdx.y + 1) / gridDim.y : KS;
+    const int64_t s0 = z0 + (z1 - z0) * wave / WAVES;
+    const int64_t nst = z0 + (z1 - z0) * (wave + 1) / WAVES - s0;
+    if (tid == 0)
+        *(u32x4*)(lds + ZERO) = u32x4{0u, 0u, 0u, 0u};
+
+    // Copy lanes: instruction i fetches rows 8i + lane/8; the lane's physical
+    // chunk lane%8 holds the row's logical chunk sk_swz(row, lane%8).  Rows
+    // past M or N and stages past the wave's range read through an
+    // out-of-range offset (zeros).  The host guarantees every valid offset,
+    // plus the stage offsets the ring forms, stays below 2^31.
+    const i32x4_t ra = make_rsrc(p.A);
+    const i32x4_t rb = make_rsrc(p.B + n0 * p.ldb * 2);
+    uint32_t vb[2], va[AI];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t r = 8u * i + lane / 8u;
+        vb[i] = n0 + r < N ? r * (uint32_t)p.ldb * 2u + sk_swz(r, lane % 8u) * 16u : kOutOfRange;
+    }
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+        const uint32_t r = 8u * i + lane / 8u;
+        va[i] = (int64_t)r < M ? r * (uint32_t)p.lda * 2u + sk_swz(r, lane % 8u) * 16u : kOutOfRange;
+    }
+    const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(lds)) + wave * (RING * SLOT);
+    auto issue = [&](int64_t st, uint32_t slot) __attribute__((always_inline)) {
+        const uint32_t past = st < nst ? 0u : kOutOfRange;
+        const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((s0 + st) * kSkRow));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            load_lds_1k_at(rb, slot + i * 1024, vb[i] | past, soff);
+#pragma unroll
+        for (int i = 0; i < AI; ++i)
+            load_lds_1k_at(ra, slot + kSkCols * kSkRow + i * 1024, va[i] | past, soff);
+    };
+
+    // two accumulators (the two 32-k halves of a stage)
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    const uint32_t c16 = lane & 15u, h = lane >> 4;
+    const bool arow = c16 < 8u * AI;  // this lane's A row is held in the slot
+    const uint32_t lbase = wave * (RING * SLOT);
+    auto compute = [&](uint32_t cur) __attribute__((always_inline)) {
+        const uint32_t slot = lbase + cur * SLOT;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint32_t c = 4u * s + h;
+            const u32x4 a = lds128(lds, arow ? slot + (kSkCols + c16) * kSkRow + (sk_swz(c16, c) << 4) : (uint32_t)ZERO);
+            const u32x4 b = lds128(lds, slot + c16 * kSkRow + (sk_swz(c16, c) << 4));
+            acc[s] = Mfma16<E>::run(b, a, acc[s]);
+        }
+    };
+
+    __syncthreads();  // the zero block is written
+    if (nst > 0) {
+#pragma unroll
+        for (int r = 0; r < RING - 1; ++r)
+            issue(r, ring + r * SLOT);
+        uint32_t cur = 0;  // slot of stage st
+        for (int64_t st = 0; st < nst; ++st) {
+            const uint32_t nxt = cur >= 1 ? cur - 1 : RING - 1;  // slot of stage st+RING-1 == slot of st-1
+            issue(st + RING - 1, ring + nxt * SLOT);
+            wait_copies<(RING - 1) * PER>();  // this wave's copies of stage st have landed
+            __builtin_amdgcn_sched_barrier(0);
+            compute(cur);
+            __builtin_amdgcn_sched_barrier(0);
+            cur = cur + 1 == RING ? 0 : cur + 1;
+        }
+    }
+    wait_copies<0>();  // the trailing zero stages land before LDS is reused
+
+    // the K tail (K % 64: at most two 32-wide blocks, the last one partial),
+    // taken by one wave of the workgroup that holds the end of K
+    if (K % kSkKE != 0 && wave == WAVES - 1 && (!SPLIT || blockIdx.y == gridDim.y - 1)) {
+        for (int64_t kb = KS * 2; kb * 32 < K; ++kb) {
+            const int64_t k = kb * 32 + h * 8;
+            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+            if ((int64_t)c16 < M && k < K) {
+                const uint8_t* src = p.A + ((int64_t)c16 * p.lda + k) * 2;
+                a = (k + 8 <= K) ? ldg128(src) : load_chunk_partial<2>(src, K - k);
+            }
+            if (n0 + c16 < N && k < K) {
+                const uint8_t* src = p.B + ((n0 + c16) * p.ldb + k) * 2;
+                b = (k + 8 <= K) ? ldg128(src) : load_chunk_partial<2>(src, K - k);
+            }
+            acc[0] = Mfma16<E>::run(b, a, acc[0]);
+        }
+    }
+    mfma_drain();
+
+    // partial tiles: value v of lane l is row l%16, column 4*(l/16) + v
+    __syncthreads();
+    float* red = (float*)lds;  // [wave][v][lane]
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        red[(wave * 4 + v) * 64 + lane] = acc[0][v] + acc[1][v];
+    __syncthreads();
+    if (wave == 0) {  // sum over the K split, in wave order
+        OutT* C = (OutT*)p.C;
+        const int64_t r = c16;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float sum = red[v * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w)
+                sum += red[(w * 4 + v) * 64 + lane];
+            const int64_t col = n0 + 4 * h + v;
+            if (r < M && col < N) {
+                if constexpr (SPLIT)
+                    atomicAdd((float*)p.C + r * p.ldc + col, sum);
+                else
+                    C[r * p.ldc + col] = convert_out<O>(sum);
+            }
+        }
+    }
+}
+
+// Whether every buffer offset of skinny_gemm stays below the descriptor's
+// range: the largest row offset of A (16 rows) and of a column block of B
+// (16 rows), plus the stage offsets the ring forms (up to RING stages past
+// the end of K).
+inline bool skinny_offsets_fit(int64_t K, int64_t lda, int64_t ldb, int ring)
+{
+    const int64_t span = K * 2 + (int64_t)ring * kSkRow + kSkRow;
+    const int64_t lim = (int64_t)kNumRecords;
+    return 16 * lda * 2 + span < lim && 16 * ldb * 2 + span < lim;
+}
+
+}  // namespace tg

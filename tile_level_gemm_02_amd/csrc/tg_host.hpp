@@ -7,6 +7,7 @@
 
 #include "tg.h"
 #include "tg_gemm_nt.hpp"
+#include "tg_gemm_skinny.hpp"
 #include "tg_kernels.hpp"
 
 namespace tg {
@@ -158,16 +159,40 @@ tg_status launch_dense(TileArgs& a, int c_dtype, hipStream_t s)
     }
 }
 
-// Workgroups per column block of the skinny kernel: enough for 256 CUs when
-// N alone gives fewer, keeping at least four 32-wide K blocks per wave.
+// Launch shape of the skinny kernel: waves per workgroup (each streams its
+// own K range) and LDS ring slots per wave.
+struct SkinnyCfg {
+    static constexpr int WAVES = 8, RING = 2;
+};
+
+// Workgroups per column block of the skinny kernel: two workgroups per CU
+// (512) when N alone gives fewer, keeping at least two 64-wide K stages per
+// wave.
 inline int skinny_split(int64_t blocks, int64_t K)
 {
-    const int64_t kb = (K + 31) / 32;
-    int64_t split = (256 + blocks - 1) / blocks;
-    const int64_t most = kb / (8 * 4);
+    int64_t split = (512 + blocks - 1) / blocks;
+    const int64_t most = K / kSkKE / (SkinnyCfg::WAVES * 2);
     if (split > most)
         split = most;
     return split > 1 ? (int)split : 1;
+}
+
+template <int E, int O, int AI, bool SPLIT>
+void launch_skinny_ai(const SkinnyArgs& sa, int64_t blocks, int split, hipStream_t s)
+{
+    typedef SkinnyCfg G;
+    hipLaunchKernelGGL((skinny_gemm<E, O, G::WAVES, AI, G::RING, SPLIT>), dim3((uint32_t)blocks, (uint32_t)split),
+                       dim3(64 * G::WAVES), 0, s, sa);
+}
+
+// A rows are copied 8 at a time: one copy instruction for M <= 8, two above.
+template <int E, int O, bool SPLIT = false>
+void launch_skinny(const SkinnyArgs& sa, int64_t blocks, int split, hipStream_t s)
+{
+    if (sa.M <= 8)
+        launch_skinny_ai<E, O, 1, SPLIT>(sa, blocks, split, s);
+    else
+        launch_skinny_ai<E, O, 2, SPLIT>(sa, blocks, split, s);
 }
 
 // fp16 / bf16 GEMM.  M <= 16 against a K-contiguous B takes the skinny
@@ -182,10 +207,10 @@ tg_status gemm_16bit(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     if (st != TG_OK || empty)
         return st;
     hipStream_t s = (hipStream_t)stream;
-    if (M <= 16 && b_layout == TG_COL_MAJOR && K > 0) {
+    typedef SkinnyCfg G;
+    if (M <= 16 && b_layout == TG_COL_MAJOR && K > 0 && skinny_offsets_fit(K, lda, ldb, G::RING)) {
         SkinnyArgs sa{M, N, K, (const uint8_t*)A, lda, (const uint8_t*)B, ldb, C, ldc};
-        constexpr int NT = 2, UNR = 8;
-        const int64_t blocks = (N + 16 * NT - 1) / (16 * NT);
+        const int64_t blocks = (N + kSkCols - 1) / kSkCols;
         if (blocks > 0x7FFFFFFF)
             return TG_ERR_NOT_SUPPORTED;
         const int split = skinny_split(blocks, K);
@@ -193,20 +218,13 @@ tg_status gemm_16bit(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
             const int64_t total = M * N;
             const int64_t zb = (total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024;
             hipLaunchKernelGGL(zero_f32<>, dim3((uint32_t)zb), dim3(256), 0, s, (float*)C, M, N, ldc);
-            hipLaunchKernelGGL((skinny_gemm<E, O_F32, 8, NT, UNR, true>), dim3((uint32_t)blocks, (uint32_t)split),
-                               dim3(512), 0, s, sa);
+            launch_skinny<E, O_F32, true>(sa, blocks, split, s);
             return launched();
         }
         switch (c_dtype) {
-        case TG_F32:
-            hipLaunchKernelGGL((skinny_gemm<E, O_F32, 8, NT, UNR>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
-            break;
-        case TG_F16:
-            hipLaunchKernelGGL((skinny_gemm<E, O_F16, 8, NT, UNR>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
-            break;
-        default:
-            hipLaunchKernelGGL((skinny_gemm<E, O_BF16, 8, NT, UNR>), dim3((uint32_t)blocks), dim3(512), 0, s, sa);
-            break;
+        case TG_F32: launch_skinny<E, O_F32>(sa, blocks, 1, s); break;
+        case TG_F16: launch_skinny<E, O_F16>(sa, blocks, 1, s); break;
+        default: launch_skinny<E, O_BF16>(sa, blocks, 1, s); break;
         }
         return launched();
     }

@@ -6,13 +6,6 @@
 //                核心抽象与编程模型对比): grid of output tiles, global->LDS copy
 //                of one K slice of A and of B per step, tile product into a
 //                cleared register accumulator, pipelined K loop, one store.
-//  skinny_gemm : M <= 16 rows against a K-contiguous B.  The B stream from HBM
-//                is the whole cost, so there is no LDS staging of B: each lane
-//                loads its MFMA operand straight from global memory with
-//                128-bit loads; the waves of a workgroup split K and reduce
-//                their partial tiles through LDS (the intra-block split-K of
-//                the TileScale README's GEMM example, section "Example of
-//                GEMM", where two warpgroups split K and all-reduce on chip).
 //  dequant_w4  : the int4 -> fp16 dequant step alone, using the very routine
 //                the w4a16 GEMM uses.
 #pragma once
@@ -318,123 +311,6 @@ template <> struct Mfma16<E_BF16> {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast<bf16x8>(a), bit_cast<bf16x8>(b), c, 0, 0, 0);
     }
 };
-
-// SPLIT: the K blocks are also split over gridDim.y workgroups per column
-// block (for narrow N, where N / (16*NT) workgroups leave most CUs idle);
-// each adds its partial tile into the fp32 output, which the host has zeroed
-// (fp32 atomic adds, so the summation order over the split is not fixed).
-template <int E, int O, int WAVES, int NT, int UNR, bool SPLIT = false>
-__global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
-{
-    typedef typename OutInfo<O>::T OutT;
-    static_assert(!SPLIT || O == O_F32, "partial tiles are added in fp32");
-    __shared__ float red[WAVES][NT][4][64];
-
-    const uint32_t tid = threadIdx.x, lane = tid & 63u, wave = tid >> 6;
-    const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t n0 = (int64_t)blockIdx.x * (16 * NT);
-    const int64_t row = lane & 15u;
-    const int64_t koff = (int64_t)(lane >> 4) * 8;  // element offset inside a 32-wide K block
-    const int64_t KB = (K + 31) / 32;
-    // this workgroup's K blocks [z0, z1), split over its waves
-    const int64_t z0 = SPLIT ? KB * blockIdx.y / gridDim.y : 0;
-    const int64_t z1 = SPLIT ? KB * (blockIdx.y + 1) / gridDim.y : KB;
-    const int64_t kb0 = z0 + (z1 - z0) * wave / WAVES, kb1 = z0 + (z1 - z0) * (wave + 1) / WAVES;
-    const bool rok = row < M;
-    const uint8_t* aptr = p.A + (rok ? row : 0) * p.lda * 2;
-    bool cok[NT];
-    const uint8_t* bptr[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const int64_t col = n0 + 16 * t + (lane & 15u);
-        cok[t] = col < N;
-        bptr[t] = p.B + (cok[t] ? col : 0) * p.ldb * 2;
-    }
-
-    // Each lane's A fragment (row l%16, 8 k) serves the NT column tiles.
-    f32x4 acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 a0[UNR], a1[UNR], b0[UNR][NT], b1[UNR][NT];
-    auto load_group = [&](u32x4 (&a)[UNR], u32x4 (&b)[UNR][NT], int64_t kb) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int64_t k = (kb + u) * 32 + koff;  // whole 16-byte chunks: the block is full
-            a[u] = rok ? ldg128(aptr + k * 2) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                b[u][t] = cok[t] ? ldg128(bptr[t] + k * 2) : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto mma_group = [&](u32x4 (&a)[UNR], u32x4 (&b)[UNR][NT]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < UNR; ++u)
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                acc[t] = Mfma16<E>::run(a[u], b[u][t], acc[t]);
-    };
-
-    // Whole blocks in groups of UNR, double-buffered: the loads of the next
-    // group are in flight while the MFMAs of this one run.
-    const int64_t kfull = K / 32 < kb1 ? K / 32 : kb1;  // blocks [kb0, kfull) hold no K tail
-    const int64_t ngroups = kfull > kb0 ? (kfull - kb0) / UNR : 0;
-    if (ngroups > 0) {
-        load_group(a0, b0, kb0);
-        for (int64_t g = 0; g < ngroups; g += 2) {
-            if (g + 1 < ngroups)
-                load_group(a1, b1, kb0 + (g + 1) * UNR);
-            mma_group(a0, b0);
-            if (g + 1 < ngroups) {
-                if (g + 2 < ngroups)
-                    load_group(a0, b0, kb0 + (g + 2) * UNR);
-                mma_group(a1, b1);
-            }
-        }
-    }
-    // remaining blocks of this wave, the K tail masked element by element
-    for (int64_t kb = kb0 + ngroups * UNR; kb < kb1; ++kb) {
-        const int64_t k = kb * 32 + koff;
-        u32x4 a = {0u, 0u, 0u, 0u};
-        if (rok && k < K)
-            a = (k + 8 <= K) ? ldg128(aptr + k * 2) : load_chunk_partial<2>(aptr + k * 2, K - k);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            u32x4 b = {0u, 0u, 0u, 0u};
-            if (cok[t] && k < K)
-                b = (k + 8 <= K) ? ldg128(bptr[t] + k * 2) : load_chunk_partial<2>(bptr[t] + k * 2, K - k);
-            acc[t] = Mfma16<E>::run(a, b, acc[t]);
-        }
-    }
-
-    mfma_drain();
-    // partial tiles of this wave: value v of lane l is row 4*(l/16) + v, column l%16
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            red[wave][t][v][lane] = acc[t][v];
-    __syncthreads();
-    if (wave < NT) {  // wave t sums tile t over the K split, in wave order
-        const int t = (int)wave;
-        const int64_t col = n0 + 16 * t + (lane & 15u);
-        OutT* C = (OutT*)p.C;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float s = red[0][t][v][lane];
-#pragma unroll
-            for (int w = 1; w < WAVES; ++w)
-                s += red[w][t][v][lane];
-            const int64_t r = (int64_t)(lane >> 4) * 4 + v;
-            if (r < M && col < N) {
-                if constexpr (SPLIT)
-                    atomicAdd((float*)p.C + r * p.ldc + col, s);
-                else
-                    C[r * p.ldc + col] = convert_out<O>(s);
-            }
-        }
-    }
-}
 
 // Zero an M x N fp32 matrix with leading dimension ldc (the split skinny
 // GEMM adds its partial tiles into it).  A template only so that every
