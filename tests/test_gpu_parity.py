@@ -302,9 +302,10 @@ def test_w4a16_layouts(tg, case):
     assert ok, (case, r, idx)
 
 
-# M <= 16: the decode kernels.  K a multiple of 2048 (M <= 4, eight waves)
-# or 1024 (M > 4, four waves) takes the LDS-ring kernel (one instantiation
-# per A copy count: M <= 2, 4, 8, 16; a single stage per wave and several);
+# M <= 16: the decode kernels.  K a multiple of 1024 (four waves) takes the
+# LDS-ring kernel (one instantiation per A copy count: M <= 2, 4, 8, 16; 16
+# columns per workgroup for M <= 4, 32 above; a single stage per wave and
+# several);
 # other K the register kernel (eight waves split the 128-K groups: a group
 # count below, equal to and not a multiple of the wave count).  Ragged N,
 # both ends of the zero-point range.

@@ -455,27 +455,27 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4(TileArgs p)
 // inside each MFMA is that of skinny_w4 (a lane's four words and its A
 // chunks cover the same 32 k).
 // --------------------------------------------------------------------------
-constexpr int kW4dCols = 32;
-template <int AI> struct W4dLayout {
-    static constexpr int QB = kW4dCols * 128, AB = 2 * AI * 512, SB = 256;
+template <int AI, int NT> struct W4dLayout {
+    static constexpr int COLS = 16 * NT;  // columns per workgroup
+    static constexpr int QB = COLS * 128, AB = 2 * AI * 512, SB = 256;
     static constexpr int SLOT = QB + AB + SB;
 };
 
-template <int AI, int WAVES, int RING>
+template <int AI, int WAVES, int RING, int NT = 2>
 __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
 {
-    typedef W4dLayout<AI> L;
-    constexpr int SLOT = L::SLOT, QB = L::QB, AB = L::AB;
-    constexpr int PER = 4 + AI + 1;  // copy instructions per stage: words, A rows, scales
+    typedef W4dLayout<AI, NT> L;
+    constexpr int SLOT = L::SLOT, QB = L::QB, AB = L::AB, COLS = L::COLS;
+    constexpr int PER = 2 * NT + AI + 1;  // copy instructions per stage: words, A rows, scales
     constexpr int ZERO = WAVES * RING * SLOT;  // 16 zero bytes shared by every wave
-    static_assert(ZERO + 16 <= 160 * 1024 && WAVES * 2 * 4 * 64 * 4 <= ZERO, "LDS");
+    static_assert(ZERO + 16 <= 160 * 1024 && WAVES * NT * 4 * 64 * 4 <= ZERO, "LDS");
     static_assert(AI >= 1 && AI <= 8 && RING >= 2 && (RING - 1) * PER <= 63, "copy ring");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[ZERO + 16];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t n0 = (int64_t)blockIdx.x * kW4dCols;
+    const int64_t n0 = (int64_t)blockIdx.x * COLS;
     const int64_t KG = K / 128;  // a multiple of 2*WAVES: every wave gets whole stages
     const int64_t g0 = KG * wave / WAVES, nst = KG / (2 * WAVES);
     uint8_t* ring = lds + wave * (RING * SLOT);
@@ -489,9 +489,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
     // lane%8 holding logical chunk (lane%8) ^ ((column/2)%8); A -- instruction
     // i, row 2i + lane/32, physical chunk lane%32 holding logical chunk
     // (lane%32) ^ row; scales -- lane l < 32 takes the two of column l
-    uint32_t vq[4], va[AI];
+    uint32_t vq[2 * NT], va[AI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2 * NT; ++i) {
         const uint32_t col = 8u * i + lane / 8u;
         const uint32_t chunk = (lane % 8u) ^ ((col >> 1) & 7u);
         vq[i] = n0 + col < N ? col * (uint32_t)p.ldq * 4u + chunk * 16u : kOutOfRange;
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
         const uint32_t chunk = (lane % 32u) ^ row;
         va[i] = (int64_t)row < M ? row * (uint32_t)p.lda * 2u + chunk * 16u : kOutOfRange;
     }
-    const uint32_t vs = (lane < 32u && n0 + lane < N) ? lane * (uint32_t)p.lds * 2u : kOutOfRange;
+    const uint32_t vs = (lane < (uint32_t)COLS && n0 + lane < N) ? lane * (uint32_t)p.lds * 2u : kOutOfRange;
 
     // stage st of this wave (groups g0 + 2st, +1) into ring slot `slot`;
     // a stage past the last one reads zeros (out-of-range offsets)
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
         const uint32_t past = st < nst ? 0u : kOutOfRange;
         const uint32_t g = (uint32_t)(g0 + 2 * st);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2 * NT; ++i)
             load_lds_1k(rq, slot + i * 1024, vq[i] | past, g * 64u);
 #pragma unroll
         for (int i = 0; i < AI; ++i)
@@ -519,9 +519,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
     };
 
     const W4Consts wc = w4_consts(p.zero_point);
-    f32x4 acc[2][2];
+    f32x4 acc[NT][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NT; ++t)
         acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t c = lane & 15u, h = lane >> 4;  // MFMA lane: column (or row) c, quarter h
     const bool arow = c < 2u * AI;                  // this lane's A row is held in the slot
@@ -529,10 +529,10 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
     auto compute = [&](const uint8_t* slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            u32x4 q[2];
-            _Float16 sc[2];
+            u32x4 q[NT];
+            _Float16 sc[NT];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < NT; ++t) {
                 const uint32_t col = 16u * t + c;
                 const uint32_t phys = (4u * u + h) ^ ((col >> 1) & 7u);
                 q[t] = lds128(slot, col * 128u + phys * 16u);
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
                 const uint32_t phys = (16u * u + 4u * h + j) ^ c;
                 const u32x4 a = lds128(lds, arow ? (uint32_t)(slot - lds) + QB + c * 512u + phys * 16u : (uint32_t)ZERO);
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < NT; ++t)
                     acc[t][j & 1] = Mfma16<E_F16>::run(a, dequant_w4_word(q[t][j], wc, f16x2{sc[t], sc[t]}), acc[t][j & 1]);
             }
         }
@@ -572,13 +572,12 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
     __syncthreads();
     float* red = (float*)lds;  // [wave][tile][v][lane]
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            red[((wave * 2 + t) * 4 + v) * 64 + lane] = acc[t][0][v] + acc[t][1][v];
+            red[((wave * NT + t) * 4 + v) * 64 + lane] = acc[t][0][v] + acc[t][1][v];
     __syncthreads();
-    if (wave < 2) {  // wave t sums tile t over the K split, in wave order
-        const int t = (int)wave;
+    for (int t = (int)wave; t < NT; t += WAVES) {  // wave t sums tile t over the K split, in wave order
         const int64_t col = n0 + 16 * t + c;
         uint16_t* C = (uint16_t*)p.C;
 #pragma unroll
@@ -586,7 +585,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
             float sum = red[(t * 4 + v) * 64 + lane];
 #pragma unroll
             for (int w = 1; w < WAVES; ++w)
-                sum += red[((w * 2 + t) * 4 + v) * 64 + lane];
+                sum += red[((w * NT + t) * 4 + v) * 64 + lane];
             const int64_t r = (int64_t)h * 4 + v;
             if (r < M && col < N)
                 C[r * p.ldc + col] = convert_out<O_F16>(sum);

@@ -215,9 +215,7 @@ tg_status gemm_16bit(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
             return TG_ERR_NOT_SUPPORTED;
         const int split = skinny_split(blocks, K);
         if (split > 1 && c_dtype == TG_F32) {  // narrow N: split K over workgroups too
-            const int64_t total = M * N;
-            const int64_t zb = (total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024;
-            hipLaunchKernelGGL(zero_f32<>, dim3((uint32_t)zb), dim3(256), 0, s, (float*)C, M, N, ldc);
+            hipLaunchKernelGGL(zero_f32<>, dim3((uint32_t)((N + 1023) / 1024), (uint32_t)M), dim3(256), 0, s, (float*)C, N, ldc);
             launch_skinny<E, O_F32, true>(sa, blocks, split, s);
             return launched();
         }

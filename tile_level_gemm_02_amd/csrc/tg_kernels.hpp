@@ -313,14 +313,20 @@ template <> struct Mfma16<E_BF16> {
 };
 
 // Zero an M x N fp32 matrix with leading dimension ldc (the split skinny
-// GEMM adds its partial tiles into it).  A template only so that every
-// translation unit that launches it may define it.
+// GEMM adds its partial tiles into it); rows start 16-byte aligned.  Grid:
+// ceil(N / 1024) x M workgroups, 4 columns per lane.  A template only so
+// that every translation unit that launches it may define it.
 template <int = 0>
-__global__ __launch_bounds__(256) void zero_f32(float* C, int64_t M, int64_t N, int64_t ldc)
+__global__ __launch_bounds__(256) void zero_f32(float* C, int64_t N, int64_t ldc)
 {
-    const int64_t total = M * N;
-    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256)
-        C[(t / N) * ldc + t % N] = 0.0f;
+    const int64_t col = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    float* row = C + (int64_t)blockIdx.y * ldc;
+    if (col + 4 <= N) {
+        *(f32x4*)(row + col) = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+        for (int64_t c = col; c < N; ++c)
+            row[c] = 0.0f;
+    }
 }
 
 // --------------------------------------------------------------------------

@@ -67,33 +67,27 @@ bool w4_skinny_eligible(const tg::TileArgs& a, int cols)
     return a.M * a.lda * 2 + a.K * 2 < lim && cols * a.ldq * 4 + a.K / 2 < lim && cols * a.lds * 2 + a.K / 64 < lim;
 }
 
+// Launch shape of skinny_w4_lds for AI A-copy instructions per stage: four
+// waves with a two-slot ring each (a stage in flight while the previous one
+// is multiplied), 16 columns per workgroup when A is at most 4 rows and 32
+// above, where the A copies, shared by the workgroup's columns, cost more
+// than the extra workgroups gain (measured at N = K = 8192).
+template <int AI> struct W4dCfg {
+    static constexpr int WAVES = 4, RING = 2, NT = AI <= 2 ? 1 : 2;
+};
+
 // skinny_w4_lds: whole stages of two scale groups per wave (K a multiple of
 // 2 * 128 * waves), scales copied as aligned 4-byte pairs, and the same
-// buffer-offset bound as skinny_w4 for its 16 A rows and 32 columns.
-bool w4_skinny_lds_eligible(const tg::TileArgs& a, int waves)
+// buffer-offset bound as skinny_w4 for its 16 A rows and `cols` columns,
+// with the stage offsets the ring forms past the end of K.
+bool w4_skinny_lds_eligible(const tg::TileArgs& a, int waves, int cols, int ring)
 {
     if (a.K <= 0 || a.K % (256 * waves) != 0 || ((uintptr_t)a.scales & 3u) != 0 || (a.lds & 1) != 0)
         return false;
     const int64_t lim = (int64_t)tg::kNumRecords;
-    return 16 * a.lda * 2 + a.K * 2 < lim && tg::kW4dCols * a.ldq * 4 + a.K / 2 < lim &&
-           tg::kW4dCols * a.lds * 2 + a.K / 64 < lim;
-}
-
-// ring depth: as many slots as fit the LDS with WAVES waves
-template <int AI, int WAVES>
-constexpr int w4d_ring()
-{
-    constexpr int r = (160 * 1024 - 16) / (WAVES * tg::W4dLayout<AI>::SLOT);
-    constexpr int rmax = 63 / (4 + AI + 1) + 1;
-    return r < rmax ? r : rmax;
-}
-
-// eight waves (two per SIMD) where the LDS still holds three slots for each,
-// else four with a deeper ring
-template <int AI>
-constexpr int w4d_waves()
-{
-    return w4d_ring<AI, 8>() >= 3 ? 8 : 4;
+    const int64_t past = 2 * (int64_t)ring;  // groups past the end of K
+    return 16 * a.lda * 2 + (a.K + past * 128) * 2 < lim && cols * a.ldq * 4 + (a.K + past * 128) / 2 < lim &&
+           cols * a.lds * 2 + (a.K / 128 + past) * 2 < lim;
 }
 
 // launches the LDS decode kernel for AI A-copy instructions per stage, or
@@ -101,15 +95,17 @@ constexpr int w4d_waves()
 template <int AI>
 bool launch_skinny_lds(const tg::TileArgs& a, hipStream_t s, tg_status* st)
 {
-    constexpr int WAVES = w4d_waves<AI>(), RING = w4d_ring<AI, WAVES>();
-    if (!w4_skinny_lds_eligible(a, WAVES))
+    typedef W4dCfg<AI> G;
+    constexpr int COLS = tg::W4dLayout<AI, G::NT>::COLS;
+    if (!w4_skinny_lds_eligible(a, G::WAVES, COLS, G::RING))
         return false;
-    const int64_t blocks = (a.N + tg::kW4dCols - 1) / tg::kW4dCols;
+    const int64_t blocks = (a.N + COLS - 1) / COLS;
     if (blocks > 0x7FFFFFFF) {
         *st = TG_ERR_NOT_SUPPORTED;
         return true;
     }
-    hipLaunchKernelGGL((tg::skinny_w4_lds<AI, WAVES, RING>), dim3((uint32_t)blocks), dim3(WAVES * 64), 0, s, a);
+    hipLaunchKernelGGL((tg::skinny_w4_lds<AI, G::WAVES, G::RING, G::NT>), dim3((uint32_t)blocks), dim3(G::WAVES * 64), 0,
+                       s, a);
     *st = tg::launched();
     return true;
 }
