@@ -107,10 +107,13 @@ inline bool nt_eligible(const TileArgs& a)
 }
 
 // Staging of the NT kernel: bytes of K per staged row, and LDS half-stages in
-// the ring.  Four (two full stages) measured faster than five on the 256 x 256
-// tile at 4096^3 (the fifth fills the LDS: 5 x 32 KB).
+// the ring.  For 16-bit inputs four (two full stages) measured faster than
+// five on the 256 x 256 tile at 4096^3 (the fifth fills the LDS: 5 x 32 KB);
+// fp8 at 8192^3, whose copies miss L2 more often and wait longer, runs ~9%
+// faster with the fifth.
 template <int E> struct NtStaging { static constexpr int RB = 128; };
-template <int BM> struct NtRing { static constexpr int NH = 4; };
+template <int E, int BM> struct NtRing { static constexpr int NH = 4; };
+template <> struct NtRing<E_FP8, 256> { static constexpr int NH = 5; };
 
 // Waves of the NT kernel per tile: the 256 x 256 tile takes 8 (2 x 4, two
 // per SIMD) for the LDS read rate its fragments need; smaller tiles take 4.
@@ -123,7 +126,7 @@ tg_status launch_nt(const TileArgs& a, hipStream_t s)
     const int64_t tiles = n_tiles<BM, BN>(a.M, a.N);
     if (tiles > 0x7FFFFFFF)
         return TG_ERR_NOT_SUPPORTED;
-    constexpr int RB = NtStaging<E>::RB, NH = NtRing<BM>::NH;
+    constexpr int RB = NtStaging<E>::RB, NH = NtRing<E, BM>::NH;
     constexpr int WM = NtWaves<BM, BN>::WM, WN = NtWaves<BM, BN>::WN;
     hipLaunchKernelGGL((gemm_nt<E, O, BM, BN, RB, NH, WM, WN>), dim3((uint32_t)tiles), dim3(64 * WM * WN), 0, s, a);
     return launched();
