@@ -150,6 +150,15 @@ __device__ __forceinline__ u32x4 lds128(const uint8_t* lds, uint32_t off)
     return *(const u32x4*)(lds + off);
 }
 
+// Store of output data that this kernel never reads back, marked non-temporal
+// (streaming): measured ~1% faster than a plain store for the 32 MB bf16
+// output of the 4096^3 GEMM.
+template <typename T>
+__device__ __forceinline__ void store_nt(T* p, T v)
+{
+    __builtin_nontemporal_store(v, p);
+}
+
 // ------------------------------------------------------------ int4 dequant
 // Eight int4 weights of one 32-bit word -> eight fp16 values, in k order
 // (nibble j, bits 4j..4j+3, is k offset j), W = fp16_RNE((q - zp) * s).

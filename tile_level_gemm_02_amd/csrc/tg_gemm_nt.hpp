@@ -354,7 +354,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
                                      out_val(i, j, 4 * g + 3)};
                     if (row < M) {
                         if (col + 4 <= N) {
-                            *(f32x4*)(C + row * p.ldc + col) = q;
+                            store_nt((f32x4*)(C + row * p.ldc + col), q);
                         } else {
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
             const int64_t row = wrow0 + r, col = wcol0 + c * 8;
             if (row < M) {
                 if (col + 8 <= N) {
-                    *(u32x4*)(C + row * p.ldc + col) = q;
+                    store_nt((u32x4*)(C + row * p.ldc + col), q);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)

@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2
         const int64_t row = wrow0 + r, col = wcol0 + c * 8;
         if (row < M) {
             if (col + 8 <= N) {
-                *(u32x4*)(C + row * p.ldc + col) = q;
+                store_nt((u32x4*)(C + row * p.ldc + col), q);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
