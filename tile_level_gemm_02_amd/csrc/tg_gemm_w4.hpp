@@ -87,12 +87,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2
     constexpr int ASTAGE = BM * RB;
     constexpr int WSTAGE = 4 * 2048; // per step: 4 waves x 32 columns x 64 bytes of words
     constexpr int CPS = AI + 2;      // copy instructions per wave per group step
-    constexpr int PER = NA / 2;      // ring steps per group
-    // at the barrier opening group step k: the copies of step k were issued
-    // PER-1 group steps earlier; those of the PER-2 group steps after it may fly
-    constexpr int WAIT_BAR = (PER - 2) * CPS;
-    static_assert(BM % 64 == 0 && NA % 2 == 0 && PER >= 2 && (PER - 1) * CPS <= 63,
-                  "tile / ring depth / copies in flight");
+    static_assert(BM % 64 == 0 && NA == 4 && CPS <= 63, "tile / ring of two slots per group");
     typedef u32x4 Frag;
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds_a[NA * ASTAGE];
@@ -152,7 +147,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2
     // slots), this lane's 16 words and the step's scale
     const uint32_t lcol = lane & 31u, lhalf = lane >> 5;
     const uint32_t lsw = lcol % CH;
-    Frag fa[2][TM];
+    Frag fa[4][TM];  // A fragments of sub-steps s .. s+2 in flight: slot s % 4
     u32x4 words[2];
     uint32_t scale;
     auto read_a = [&](uint32_t slot, int s, int fs) __attribute__((always_inline)) {
@@ -166,7 +161,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2
         const uint8_t* ws = lds_w + slot * WSTAGE + wq * 2048;
         words[0] = lds128(ws, lcol * 64u + lhalf * 32u);
         words[1] = lds128(ws, lcol * 64u + lhalf * 32u + 16u);
-        scale = *(const uint16_t*)(lds_s + ((wq * 32u + lcol) * G + kt) * 2u);
+        scale = *(const uint16_t*)(lds_s + ((wq * 32u + lcol) * G + (kt < G ? kt : G - 1u)) * 2u);  // (clamped past the last step)
     };
     const W4Consts wc = w4_consts(p.zero_point);
     auto dequant = [&](int s) __attribute__((always_inline)) {
@@ -198,42 +193,53 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2
             load_lds_256(rs, lds_s + t * 256u, v, 0u);
         }
     }
-#pragma unroll
-    for (int u = 0; u < PER - 1; ++u)
-        copy_step(grp + 2u * u);
+    copy_step(grp);
+    copy_step(grp + 2u);
+    wait_copies<CPS>();  // this wave's copies of its group's first step (and the scales) landed
+    __syncthreads();     // ... and every wave's
 
-    // ---- group steps.  The barrier opens each one (both groups pass it
-    // together): the group's copies of the step have landed for every wave,
-    // and every read of its previous step's slot is done, so that slot is
-    // refilled right away.  Each sub-step interleaves its two MFMAs with the
-    // VALU instructions that dequantise the next word and the A reads of the
-    // next sub-step.
+    // ---- group steps.  Entering step kt, its words and scale and the A
+    // fragments of its sub-steps 0 and 1 are in registers and the B operand
+    // of sub-step 0 is dequantised.  Sub-step s issues its two MFMAs, the A
+    // reads of sub-step s+2 and the dequant of sub-step s+1's word (VALU),
+    // interleaved.  The barrier sits before the last sub-step, whose operands
+    // are all in registers: past it the copies of the group's step kt+2 have
+    // landed for every wave (published), and every read of step kt's slot is
+    // done, so the slot is refilled with step kt+4 at once and the first
+    // operands of step kt+2 are read while sub-step 7's MFMAs run.
+    read_b(grp, grp % NA);
+    read_a(grp % NA, 0, 0);
+    read_a(grp % NA, 1, 1);
+    Frag b = dequant(0);
     for (uint32_t kt = grp; kt < KT; kt += 2) {
-        const uint32_t slot = kt % NA;
-        wait_copies<WAIT_BAR>();  // this wave's copies of step kt landed (and the scales)
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        copy_step(kt + NA - 2);  // into the slot of step kt-2
-        read_b(kt, slot);
-        read_a(slot, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        Frag b = dequant(0);
+        const uint32_t slot = kt % NA, nslot = (kt + 2) % NA;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < SUB; ++s) {
-            mma(b, s & 1);
-            if (s + 1 < SUB) {
-                read_a(slot, s + 1, (s + 1) & 1);
-                b = dequant(s + 1);
-            }
+        for (int s = 0; s < SUB - 1; ++s) {
+            mma(b, s & 3);
+            if (s + 2 < SUB)
+                read_a(slot, s + 2, (s + 2) & 3);
+            b = dequant(s + 1);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (s + 2 < SUB)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        wait_copies<0>();  // this wave's copies of step kt+2 landed ...
+        __syncthreads();   // ... and every wave's; every read of step kt is done
+        __builtin_amdgcn_sched_barrier(0);
+        copy_step(kt + 4);  // into the slot of step kt (zeros past the last step)
+        // (past the group's last step these reads are stale and unused)
+        read_b(kt + 2, nslot);
+        read_a(nslot, 0, 0);
+        read_a(nslot, 1, 1);
+        mma(b, (SUB - 1) & 3);
+        __builtin_amdgcn_sched_barrier(0);
+        b = dequant(0);
     }
     wait_copies<0>();  // every copy (including those past the last step) has landed
     mfma_drain();
