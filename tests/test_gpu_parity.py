@@ -102,6 +102,19 @@ def test_dense_small(tg, dt, lay, out, shape):
     _check(C, A, B, dt, lay, out)
 
 
+# Edge shapes: M on both sides of the skinny bound (15, 17) and one short of
+# a 256 tile, N tails, K of one element, one 16-byte chunk, one step plus a
+# chunk (72) and two steps plus a chunk (136).
+@pytest.mark.parametrize("K", [1, 8, 72, 136])
+@pytest.mark.parametrize("N", [31, 257])
+@pytest.mark.parametrize("M", [15, 17, 255])
+@pytest.mark.parametrize("lay", ["row", "col"])
+def test_dense_edge_shapes(tg, lay, M, N, K):
+    A, B, _, _ = _inputs("bf16", M, N, K, lay, seed=M * 7 + N * 3 + K)
+    C = _run_dense(tg, "bf16", A, B, lay, "f32")
+    _check(C, A, B, "bf16", lay, "f32")
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 16), (17, 33, 256), (64, 130, 512), (100, 300, 1000),
                                    (300, 260, 384)], ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
