@@ -258,45 +258,48 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2
                        bit_cast<u32x4>(f32x4{acc[i][4 * v4], acc[i][4 * v4 + 1], acc[i][4 * v4 + 2], acc[i][4 * v4 + 3]}));
     }
     __syncthreads();
-    if (grp == 1)
-        return;
+    // ---- epilogue (fp16): group 0 adds group 1's partial blocks and stages
+    // the whole BM x 128 tile in LDS (256-byte rows, 16-byte chunks XOR-
+    // swizzled by row; wave quarter q writes chunks 4q .. 4q+3 of each row);
+    // then all 8 waves store whole rows, 4 rows x 256 bytes per instruction
+    // (partial-line stores cost far more).  Accumulator value v of lane l
+    // holds row 32i + l%32, column 8*(v/4) + 4*(l/32) + v%4 of the wave's
+    // 32 columns.
+    constexpr int OB = BN * 2, NCH = OB / 16, TBYTES = BM * OB;
+    static_assert(PBYTES + TBYTES <= NA * ASTAGE, "partials and staging must fit the A ring");
+    uint8_t* ep = lds_a + PBYTES;
+    if (grp == 0) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-            const f32x4 o = bit_cast<f32x4>(lds128(part, ((i * 4 + v4) * 64 + lane) * 16u));
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const f32x4 o = bit_cast<f32x4>(lds128(part, ((i * 4 + v4) * 64 + lane) * 16u));
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                acc[i][4 * v4 + e] += o[e];
-        }
-
-    // ---- epilogue (fp16, group 0): each wave stages its BM x 32 sub-tile in
-    // LDS and stores 16-byte row pieces.  Accumulator value v of lane l holds
-    // row 32i + l%32, column 8*(v/4) + 4*(l/32) + v%4 of the wave's columns.
-    constexpr int WR = BM, OB = 64, NCH = 4, WBYTES = WR * OB;
-    static_assert(PBYTES + 4 * WBYTES <= NA * ASTAGE, "partials and staging must fit the A ring");
-    const int64_t wrow0 = m0, wcol0 = n0 + wq * 32;
-    uint8_t* ep = lds_a + PBYTES + wq * WBYTES;
+                for (int e = 0; e < 4; ++e)
+                    acc[i][4 * v4 + e] += o[e];
+            }
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const uint32_t r = i * 32 + lcol;
+        for (int i = 0; i < TM; ++i) {
+            const uint32_t r = i * 32 + lcol;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const uint32_t lo = (uint32_t)f32_to_f16_rne(acc[i][4 * g]) |
-                                ((uint32_t)f32_to_f16_rne(acc[i][4 * g + 1]) << 16);
-            const uint32_t hi = (uint32_t)f32_to_f16_rne(acc[i][4 * g + 2]) |
-                                ((uint32_t)f32_to_f16_rne(acc[i][4 * g + 3]) << 16);
-            *(u32x2*)(ep + r * OB + (((uint32_t)g ^ (r % NCH)) << 4) + lhalf * 8) = u32x2{lo, hi};
+            for (int g = 0; g < 4; ++g) {
+                const uint32_t c = wq * 4u + (uint32_t)g;  // 16-byte chunk of the tile row
+                const uint32_t lo = (uint32_t)f32_to_f16_rne(acc[i][4 * g]) |
+                                    ((uint32_t)f32_to_f16_rne(acc[i][4 * g + 1]) << 16);
+                const uint32_t hi = (uint32_t)f32_to_f16_rne(acc[i][4 * g + 2]) |
+                                    ((uint32_t)f32_to_f16_rne(acc[i][4 * g + 3]) << 16);
+                *(u32x2*)(ep + r * OB + ((c ^ (r % NCH)) << 4) + lhalf * 8) = u32x2{lo, hi};
+            }
         }
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __syncthreads();  // the tile is staged
     uint16_t* C = (uint16_t*)p.C;
 #pragma unroll
-    for (int t = 0; t < WR * NCH / 64; ++t) {
-        const uint32_t idx = t * 64 + lane;
+    for (int t = 0; t < BM * NCH / kW4Threads; ++t) {
+        const uint32_t idx = t * kW4Threads + tid;
         const uint32_t r = idx / NCH, c = idx % NCH;
         const u32x4 q = lds128(ep, r * OB + ((c ^ (r % NCH)) << 4));
-        const int64_t row = wrow0 + r, col = wcol0 + c * 8;
+        const int64_t row = m0 + r, col = n0 + c * 8;
         if (row < M) {
             if (col + 8 <= N) {
                 store_nt((u32x4*)(C + row * p.ldc + col), q);
