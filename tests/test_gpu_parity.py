@@ -152,6 +152,31 @@ def test_skinny_outputs_strided(tg, out, M, K):
     assert torch.isnan(store[:, N:]).all()
 
 
+# Row-major (N-contiguous) B takes the tile kernel's transposing-read path
+# when N and K are multiples of 8: ragged tiles on every side, K tails of one
+# chunk and of several, padded leading dimensions, all outputs; and a large
+# case on sampled rows.
+@pytest.mark.parametrize("shape", [(300, 264, 200), (1000, 1288, 1032), (257, 520, 72), (64, 8, 8),
+                                   (513, 1024, 4104)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_row_major_b_nt_path(tg, dt, out, shape):
+    M, N, K = shape
+    A, B, _, _ = _inputs(dt, M, N, K, "row", seed=M + 3 * N + K)
+    C = _run_dense(tg, dt, A, B, "row", out, pad=8)
+    rows = None if M * N * K <= 2**29 else np.r_[0:8, M // 2 : M // 2 + 8, M - 8 : M]
+    _check(C, A, B, dt, "row", out, rows=rows)
+
+
+def test_row_major_b_large(tg):
+    M = N = K = 2048
+    A, B, _, _ = _inputs("bf16", M, N, K, "row", seed=77)
+    C = _run_dense(tg, "bf16", A, B, "row", "bf16")
+    _check(C, A, B, "bf16", "row", "bf16", rows=np.r_[0:8, 1020:1028, 2040:2048])
+    C2 = _run_dense(tg, "bf16", A, B, "row", "bf16")
+    assert torch.equal(C, C2), "repeated runs differ"
+
+
 # Narrow N with fp32 output (a column shard of the skinny workload): the
 # skinny kernel also splits K over workgroups and adds their partial tiles
 # into a zeroed C with fp32 atomics.  Ragged N and K, a split count that does

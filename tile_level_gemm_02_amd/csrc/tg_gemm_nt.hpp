@@ -92,7 +92,7 @@ __device__ __forceinline__ void wait_copies()
 // WM x WN waves share the tile (each computes a BM/WM x BN/WN sub-tile).
 // With 8 waves (two per SIMD) the LDS sustains about twice the fragment-read
 // rate of 4 waves (one per SIMD), which the 256 x 256 tile needs.
-template <int E, int O, int BM, int BN, int RB, int NH, int WM = 2, int WN = 2>
+template <int E, int O, int BM, int BN, int RB, int NH, int WM = 2, int WN = 2, int BL = B_KCONTIG>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
 {
     constexpr int EB = ElemInfo<E>::bytes;
@@ -113,6 +113,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     static_assert(BM == BN && AI == BI, "square tiles: A and B half-stages alike");
     static_assert(NH >= 4 && (NH - 3) * AI <= 63, "copies in flight");
     typedef typename Mfma32<E>::frag Frag;
+    // N-contiguous B (row-major K x N): a B half-stage holds the step's KE
+    // rows of k, each BN elements wide (RBN bytes, CHN chunks; the same HALF
+    // bytes), copied RPIN rows per instruction and read by the transposing
+    // LDS load (16-bit elements only)
+    constexpr bool NB = BL == B_NCONTIG;
+    static_assert(!NB || EB == 2, "N-contiguous B: 16-bit elements");
+    constexpr int RBN = BN * EB, CHN = RBN / 16, RPIN = 1024 / RBN;
+    static_assert(!NB || (KE * RBN == HALF && CHN >= 8 && (KE / RPIN) % NW == 0 && KE / RPIN / NW == BI),
+                  "N-contiguous B stage: same size and copy count as the K-contiguous one");
+    // physical chunk of logical chunk c of B row k is c ^ swn(k): the four
+    // rows k .. k+3 that one transposing read takes (32 bytes each, two
+    // 16-lane groups side by side) fall in distinct banks
+    auto swn = [](uint32_t k) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (CHN >= 16)
+            return 4u * (k % 4u);
+        else
+            return 4u * ((((k % 4u) + 1u) / 2u) % 2u);  // 128-byte rows: two rows per bank line
+    };
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NH * HALF];
 
@@ -128,7 +146,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     const int32_t rows_a = (int32_t)(M - m0 < BM ? M - m0 : BM);
     const int32_t rows_b = (int32_t)(N - n0 < BN ? N - n0 : BN);
     const i32x4_t ra = make_rsrc(p.A + m0 * (int64_t)ldab);
-    const i32x4_t rb = make_rsrc(p.B + n0 * (int64_t)ldbb);
+    const i32x4_t rb = make_rsrc(NB ? p.B + n0 * EB : p.B + n0 * (int64_t)ldbb);
     const int64_t KT = (K + KE - 1) / KE;  // K is a multiple of CE on this path
 
     // ---- staged layout: row r of a stage operand holds RB bytes of K as CH
@@ -150,8 +168,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     const uint32_t lchunk1 = (lane % CH) ^ ((4u + lrowi / RSW) % CH);
     const uint32_t va0 = (wave * (BM / NW) + lrowi) * ldab + lchunk0 * 16u;
     const uint32_t va1 = (wave * (BM / NW) + lrowi) * ldab + lchunk1 * 16u;
-    const uint32_t vb0 = (wave * (BN / NW) + lrowi) * ldbb + lchunk0 * 16u;
-    const uint32_t vb1 = (wave * (BN / NW) + lrowi) * ldbb + lchunk1 * 16u;
+    uint32_t vb0 = (wave * (BN / NW) + lrowi) * ldbb + lchunk0 * 16u;
+    uint32_t vb1 = (wave * (BN / NW) + lrowi) * ldbb + lchunk1 * 16u;
+    // N-contiguous B: instruction q of wave w copies k rows (w*BI + q)*RPIN
+    // + lane/CHN, lane i landing at physical chunk i%CHN of its row, which
+    // holds logical chunk (i%CHN) ^ swn(row) (columns 8c .. 8c+7 of the
+    // tile); the row's parity class mod 4 alternates with q only, so there
+    // is again one offset for even q and one for odd q.  Columns past N read
+    // zeros (N is a multiple of 8: no partial chunks).
+    const uint32_t lrown = lane / CHN;
+    if constexpr (NB) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t kr = (wave * BI + q) * RPIN + lrown;
+            const uint32_t lc = (lane % CHN) ^ swn(kr);
+            const uint32_t v = lrown * ldbb + lc * 16u;
+            const uint32_t oob = n0 + (int64_t)lc * CE < N ? 0u : kOutOfRange;
+            (q == 0 ? vb0 : vb1) = v | oob;
+        }
+    }
 
     // half-stage of A (or B) of K step kt
     auto a_ptr = [&](int64_t kt) __attribute__((always_inline)) -> uint8_t* {
@@ -177,8 +212,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         o0 = (h & 1) ? vb0 : va0;
         o1 = (h & 1) ? vb1 : va1;
         if constexpr (decltype(edge)::value) {
-            o0 |= chunk_oob(kt, lchunk0);
-            o1 |= chunk_oob(kt, lchunk1);
+            if (!(NB && (h & 1))) {  // (N-contiguous B: the K tail is a row check, in copy_half)
+                o0 |= chunk_oob(kt, lchunk0);
+                o1 |= chunk_oob(kt, lchunk1);
+            }
         }
         const uint32_t past = kt < KT ? 0u : kOutOfRange;
         o0 |= past;
@@ -194,6 +231,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     auto copy_half = [&](auto edge, int64_t h, int q, uint32_t o0, uint32_t o1) __attribute__((always_inline)) {
         const int64_t kt = h >> 1;
         uint32_t v = (q & 1) ? o1 : o0;
+        if (NB && (h & 1)) {  // k rows (w*BI + q)*RPIN + lane/CHN of step kt
+            const uint32_t kr = (wave * BI + (uint32_t)q) * RPIN;
+            if constexpr (decltype(edge)::value)
+                v |= kt * KE + kr + lrown < K ? 0u : kOutOfRange;
+            load_lds_1k_at(rb, half_dst(h) + q * 1024, v, ((uint32_t)kt * KE + kr) * ldbb);
+            return;
+        }
         if constexpr (decltype(edge)::value) {
             const int32_t rows = (h & 1) ? rows_b : rows_a;
             v |= (int32_t)(wave * ((h & 1) ? BN / NW : BM / NW) + RPI * q + lrowi) < rows ? 0u : kOutOfRange;
@@ -219,7 +263,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         const uint8_t* st = is_a ? a_ptr(kt) : b_ptr(kt);
         const uint32_t row0 = (is_a ? a_row0 : b_row0) + (uint32_t)idx * 32 * RB;
         Frag f;
-        if constexpr (E == E_FP8) {
+        if constexpr (NB) {
+            if (!is_a) {
+                // 8 k of column n of the block from two transposing reads (4 k
+                // each): in each 16-lane group, source lane 4e + a addresses k
+                // row (base + e), columns 4a .. 4a+3 of the group's 16, and lane
+                // 4a + j receives column 4a + j at rows base .. base+3
+                const uint32_t l16 = lane % 16u;
+                const uint32_t col = wn * (BN / WN) + (uint32_t)idx * 32u + 16u * ((lane / 16u) % 2u) + 4u * (l16 % 4u);
+                uint32_t w[4];
+#pragma unroll
+                for (int r2 = 0; r2 < 2; ++r2) {
+                    const uint32_t k = (uint32_t)(16 * s) + 8u * lgrp + 4u * (uint32_t)r2 + l16 / 4u;
+                    const uint32_t off = k * RBN + (((col / CE) ^ swn(k)) << 4) + (col % CE) * EB;
+                    const auto v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(lds_u8_t)(st + off));
+                    w[2 * r2] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+                    w[2 * r2 + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+                }
+                f = u32x4{w[0], w[1], w[2], w[3]};
+            } else {
+                f = lds128(st, row0 + ((((uint32_t)(2 * s) + lgrp) ^ sw) << 4));
+            }
+        } else if constexpr (E == E_FP8) {
             const uint32_t c0 = (uint32_t)(4 * s) + 2u * lgrp;
             const u32x4 lo = lds128(st, row0 + ((c0 ^ sw) << 4));
             const u32x4 hi = lds128(st, row0 + (((c0 + 1u) ^ sw) << 4));

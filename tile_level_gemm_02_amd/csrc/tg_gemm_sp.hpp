@@ -233,25 +233,46 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
     constexpr int WR = BM / WM, WC = BN / WN;
     const int64_t wrow0 = m0 + wm * WR, wcol0 = n0 + wn * WC;
     if constexpr (O == O_F32) {
+        // fp32 output: staged through LDS in passes of PR rows, stored as
+        // whole rows (as the NT kernel does: a lane's 4 columns stored
+        // directly make each store instruction write 32 rows x 32 bytes)
+        constexpr int OB = WC * 4, NCH = OB / 16, PBY = NS * STAGE / NW;
+        constexpr int PR = PBY / OB >= WR ? WR : (PBY / OB >= WR / 2 ? WR / 2 : WR / 4);
+        static_assert(PR % 32 == 0 && WR % PR == 0 && (PR * NCH) % 64 == 0, "fp32 staging passes");
+        __syncthreads();  // every wave is done reading the stages
+        uint8_t* ep = lds + wave * PBY;
         float* C = (float*)p.C;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int64_t row = wrow0 + i * 32 + lrow;
+        for (int pass = 0; pass < WR / PR; ++pass) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
+            for (int ii = 0; ii < PR / 32; ++ii) {
+                const int i = pass * (PR / 32) + ii;
+                const uint32_t r = ii * 32 + lrow;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int64_t col = wcol0 + j * 32 + 8 * g + 4 * h;
-                    const f32x4 q = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    if (row < M) {
-                        if (col + 4 <= N) {
-                            store_nt((f32x4*)(C + row * p.ldc + col), q);
-                        } else {
+                for (int j = 0; j < TN; ++j) {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (col + e < N)
-                                    C[row * p.ldc + col + e] = q[e];
-                        }
+                    for (int g = 0; g < 4; ++g) {
+                        const uint32_t c = (uint32_t)(8 * j + 2 * g) + h;  // columns j*32 + 8g + 4h .. +3
+                        const f32x4 q = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                        *(f32x4*)(ep + r * OB + ((c ^ (r % NCH)) << 4)) = q;
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes done
+#pragma unroll
+            for (int t = 0; t < PR * NCH / 64; ++t) {
+                const uint32_t idx = t * 64 + lane;
+                const uint32_t r = idx / NCH, c = idx % NCH;
+                const f32x4 q = bit_cast<f32x4>(lds128(ep, r * OB + ((c ^ (r % NCH)) << 4)));
+                const int64_t row = wrow0 + pass * PR + r, col = wcol0 + c * 4;
+                if (row < M) {
+                    if (col + 4 <= N) {
+                        store_nt((f32x4*)(C + row * p.ldc + col), q);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (col + e < N)
+                                C[row * p.ldc + col + e] = q[e];
                     }
                 }
             }

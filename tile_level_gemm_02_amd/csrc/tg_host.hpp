@@ -106,6 +106,20 @@ inline bool nt_eligible(const TileArgs& a)
     return (a.K % (16 / EB)) == 0 && 256 * a.lda * EB + a.K * EB < lim && 256 * a.ldb * EB + a.K * EB < lim;
 }
 
+// The NT kernel with an N-contiguous (row-major) B: 16-bit elements, whole
+// 16-byte chunks along K for A and along N for B, and 32-bit buffer offsets
+// over the K rows of B (plus the rows of the steps past K that the ring forms).
+template <int E>
+inline bool nt_eligible_nrow(const TileArgs& a)
+{
+    constexpr int EB = ElemInfo<E>::bytes;
+    if constexpr (EB != 2)
+        return false;
+    const int64_t lim = (int64_t)kNumRecords;
+    return (a.K % 8) == 0 && (a.N % 8) == 0 && 256 * a.lda * EB + a.K * EB < lim &&
+           (a.K + 6 * 64) * a.ldb * EB + 256 * EB < lim;
+}
+
 // Staging of the NT kernel: bytes of K per staged row, and LDS half-stages in
 // the ring.  For 16-bit inputs four (two full stages) measured faster than
 // five on the 256 x 256 tile at 4096^3 (the fifth fills the LDS: 5 x 32 KB);
@@ -120,7 +134,7 @@ template <> struct NtRing<E_FP8, 256> { static constexpr int NH = 5; };
 template <int BM, int BN> struct NtWaves { static constexpr int WM = 2, WN = 2; };
 template <> struct NtWaves<256, 256> { static constexpr int WM = 2, WN = 4; };
 
-template <int E, int O, int BM, int BN>
+template <int E, int O, int BM, int BN, int BL = B_KCONTIG>
 tg_status launch_nt(const TileArgs& a, hipStream_t s)
 {
     const int64_t tiles = n_tiles<BM, BN>(a.M, a.N);
@@ -128,18 +142,18 @@ tg_status launch_nt(const TileArgs& a, hipStream_t s)
         return TG_ERR_NOT_SUPPORTED;
     constexpr int RB = NtStaging<E>::RB, NH = NtRing<E, BM>::NH;
     constexpr int WM = NtWaves<BM, BN>::WM, WN = NtWaves<BM, BN>::WN;
-    hipLaunchKernelGGL((gemm_nt<E, O, BM, BN, RB, NH, WM, WN>), dim3((uint32_t)tiles), dim3(64 * WM * WN), 0, s, a);
+    hipLaunchKernelGGL((gemm_nt<E, O, BM, BN, RB, NH, WM, WN, BL>), dim3((uint32_t)tiles), dim3(64 * WM * WN), 0, s, a);
     return launched();
 }
 
-template <int E, int O>
+template <int E, int O, int BL = B_KCONTIG>
 tg_status launch_nt_sized(TileArgs& a, hipStream_t s)
 {
     a.group_m = 4;
     switch (pick_tile(a.M, a.N, true)) {
-    case 256: return launch_nt<E, O, 256, 256>(a, s);
-    case 128: return launch_nt<E, O, 128, 128>(a, s);
-    default: return launch_nt<E, O, 64, 64>(a, s);
+    case 256: return launch_nt<E, O, 256, 256, BL>(a, s);
+    case 128: return launch_nt<E, O, 128, 128, BL>(a, s);
+    default: return launch_nt<E, O, 64, 64, BL>(a, s);
     }
 }
 
@@ -152,6 +166,14 @@ tg_status launch_dense(TileArgs& a, int c_dtype, hipStream_t s)
             case TG_F32: return launch_nt_sized<E, O_F32>(a, s);
             case TG_F16: return launch_nt_sized<E, O_F16>(a, s);
             default: return launch_nt_sized<E, O_BF16>(a, s);
+            }
+        }
+    } else if constexpr (ElemInfo<E>::bytes == 2) {
+        if (nt_eligible_nrow<E>(a)) {
+            switch (c_dtype) {
+            case TG_F32: return launch_nt_sized<E, O_F32, B_NCONTIG>(a, s);
+            case TG_F16: return launch_nt_sized<E, O_F16, B_NCONTIG>(a, s);
+            default: return launch_nt_sized<E, O_BF16, B_NCONTIG>(a, s);
             }
         }
     }

@@ -279,14 +279,9 @@ __global__ __launch_bounds__(kThreads) void tile_gemm(TileArgs p)
 }
 
 // --------------------------------------------------------------------------
-// Skinny GEMM: M <= 16, B K-contiguous, 16-bit inputs.  A workgroup owns
-// 16*NT output columns; its WAVES waves split K into contiguous ranges of
-// 32-wide blocks, each running 16x16x32 MFMAs on operands loaded straight from
-// global memory (lane l: row/column l%16, k offset 8*(l/16) within the block).
-// One A fragment feeds NT column tiles, halving the A (L2) traffic per byte
-// of B at NT = 2; groups of UNR blocks are double-buffered so the next group's
-// loads are in flight during this group's MFMAs.  The partial 16x16 tiles are
-// summed through LDS in a fixed wave order (deterministic).
+// Arguments of the skinny GEMM (M <= 16 against a K-contiguous B; the kernel
+// is in tg_gemm_skinny.hpp), and the 16x16x32 matrix instruction it and the
+// w4a16 decode kernels use.
 // --------------------------------------------------------------------------
 struct SkinnyArgs {
     int64_t M, N, K;
