@@ -25,7 +25,11 @@
 //    the MFMAs of sub-step s run), 32x32 MFMAs accumulating in fp32 AGPRs;
 //    the one barrier per K step sits before the last sub-step's MFMAs, which
 //    hide its skew and the first reads of the next step;
-//  * epilogue: scale (fp8), round to the output type, masked stores.
+//  * epilogue: scale (fp8), round to the output type, staged through LDS so
+//    that every store instruction writes whole 128-byte lines;
+//  * a row-major (N-contiguous) 16-bit B is taken too (BL = B_NCONTIG): its
+//    half-stage holds the step's k rows of the tile's columns, and each B
+//    fragment comes from transposing LDS reads (ds_read_b64_tr_b16).
 #pragma once
 
 #include <type_traits>
