@@ -230,6 +230,34 @@ def test_large_ragged_16bit_out(tg, dt, out):
     _check(C, A, B, dt, "col", out, sa, sb, rows=rows)
 
 
+# Leading dimensions so large that the buffer offsets of the fast kernels
+# would pass 2^31 bytes: the host must send these calls to the generic tile
+# kernel (64-bit addresses), which must still be right.  The padded operand
+# is a few GB of device memory; only its first K (or N) columns hold data.
+@pytest.mark.parametrize("case", ["tile_a", "tile_b_col", "tile_b_row", "skinny_a", "skinny_b"])
+def test_huge_leading_dimension_fallback(tg, case):
+    big = 4_300_000  # elements: 256 rows of it exceed 2^31 bytes in 16-bit elements
+    if case.startswith("skinny"):
+        M, N, K, lay = 5, 40, 1000, "col"
+        big = 70_000_000  # 16 rows of it exceed 2^31 bytes
+    else:
+        M, N, K = 300, 264, 200
+        lay = "row" if case == "tile_b_row" else "col"
+    A, B, _, _ = _inputs("bf16", M, N, K, lay, seed=7 + len(case))
+    pad_a = big - K if case in ("tile_a", "skinny_a") else (-K) % 8
+    pad_b_cols = B.shape[1]
+    pad_b = big - pad_b_cols if case in ("tile_b_col", "tile_b_row", "skinny_b") else (-pad_b_cols) % 8
+    dA = _dev(A, pad_a)
+    dB = _dev(B, pad_b)
+    store = torch.full((M, (N + 7) // 8 * 8), float("nan"), dtype=torch.float32, device="cuda")
+    C = store[:, :N]
+    tg.tg_gemm_bf16(dA, dB, C, b_layout=lay)
+    torch.cuda.synchronize()
+    _check(C, A, B, "bf16", lay, "f32")
+    del dA, dB
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16", "fp8"])
 def test_exact_structure(tg, dt):
     """Identity and all-ones inputs have exactly representable results: bit-exact."""
