@@ -535,27 +535,36 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
     const uint32_t c = lane & 15u, h = lane >> 4;  // MFMA lane: column (or row) c, quarter h
     const bool arow = c < 2u * AI;                  // this lane's A row is held in the slot
 
+    // One stage: every LDS read first (words, scales and A chunks of both
+    // groups), so a wave pays the LDS latency once per stage instead of once
+    // per MFMA; then the dequant and the MFMAs, in the same order as before.
     auto compute = [&](const uint8_t* slot) __attribute__((always_inline)) {
+        u32x4 q[2][NT], a[2][4];
+        _Float16 sc[2][NT];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            u32x4 q[NT];
-            _Float16 sc[NT];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const uint32_t col = 16u * t + c;
                 const uint32_t phys = (4u * u + h) ^ ((col >> 1) & 7u);
-                q[t] = lds128(slot, col * 128u + phys * 16u);
-                sc[t] = bit_cast<_Float16>(*(const uint16_t*)(slot + QB + AB + col * 4u + u * 2u));
+                q[u][t] = lds128(slot, col * 128u + phys * 16u);
+                sc[u][t] = bit_cast<_Float16>(*(const uint16_t*)(slot + QB + AB + col * 4u + u * 2u));
             }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t phys = (16u * u + 4u * h + j) ^ c;
-                const u32x4 a = lds128(lds, arow ? (uint32_t)(slot - lds) + QB + c * 512u + phys * 16u : (uint32_t)ZERO);
+                a[u][j] = lds128(lds, arow ? (uint32_t)(slot - lds) + QB + c * 512u + phys * 16u : (uint32_t)ZERO);
+            }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-                    acc[t][j & 1] = Mfma16<E_F16>::run(a, dequant_w4_word(q[t][j], wc, f16x2{sc[t], sc[t]}), acc[t][j & 1]);
-            }
-        }
+                    acc[t][j & 1] = Mfma16<E_F16>::run(a[u][j], dequant_w4_word(q[u][t][j], wc, f16x2{sc[u][t], sc[u][t]}),
+                                                       acc[t][j & 1]);
     };
 
     __syncthreads();  // the zero block is written
