@@ -76,7 +76,9 @@ def test_fp8_validation(tg):
                         A16, 8, 0, None)
     assert lib.tg_gemm_fp8(*args(M=-1)) == tg.TG_ERR_INVALID_VALUE
     assert lib.tg_gemm_fp8(*args(sa=float("inf"))) == tg.TG_ERR_INVALID_VALUE
-    assert lib.tg_gemm_fp8(*args(lay=0)) == tg.TG_ERR_NOT_SUPPORTED
+    # row-major B: ldb >= N, and N bytes per row a multiple of 16
+    assert lib.tg_gemm_fp8(8, 32, 8, A16, 16, A16, 16, 0, 1.0, 1.0, A16, 32, 0, None) == tg.TG_ERR_INVALID_VALUE
+    assert lib.tg_gemm_fp8(8, 24, 8, A16, 16, A16, 24, 0, 1.0, 1.0, A16, 24, 0, None) == tg.TG_ERR_MISALIGNED
     assert lib.tg_gemm_fp8(*args(M=0)) == tg.TG_OK
     # fp8 rows of 8 elements are only 8 bytes: misaligned leading dimension
     assert lib.tg_gemm_fp8(8, 8, 8, A16, 8, A16, 16, 1, 1.0, 1.0, A16, 8, 0, None) == tg.TG_ERR_MISALIGNED

@@ -118,11 +118,24 @@ def test_dense_edge_shapes(tg, lay, M, N, K):
 @pytest.mark.parametrize("shape", [(1, 1, 16), (17, 33, 256), (64, 130, 512), (100, 300, 1000),
                                    (300, 260, 384)], ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
-def test_fp8_small(tg, out, shape):
+@pytest.mark.parametrize("lay", ["col", "row"])
+def test_fp8_small(tg, lay, out, shape):
     M, N, K = shape
-    A, B, sa, sb = _inputs("fp8", M, N, K, "col", seed=M + N + K)
-    C = _run_dense(tg, "fp8", A, B, "col", out, scale_a=sa, scale_b=sb)
-    _check(C, A, B, "fp8", "col", out, sa, sb)
+    A, B, sa, sb = _inputs("fp8", M, N, K, lay, seed=M + N + K)
+    C = _run_dense(tg, "fp8", A, B, lay, out, scale_a=sa, scale_b=sb)
+    _check(C, A, B, "fp8", lay, out, sa, sb)
+
+
+def test_fp8_row_major_b_matches_col(tg):
+    """The same fp8 product with B stored row-major and column-major: both
+    within the bound, and the oracle's two layouts give one reference."""
+    M, N, K = 520, 384, 1040
+    A, Bc, sa, sb = _inputs("fp8", M, N, K, "col", seed=77)
+    Br = Bc.t().contiguous()
+    Cc = _run_dense(tg, "fp8", A, Bc, "col", "f32", scale_a=sa, scale_b=sb)
+    Cr = _run_dense(tg, "fp8", A, Br, "row", "f32", scale_a=sa, scale_b=sb)
+    _check(Cc, A, Bc, "fp8", "col", "f32", sa, sb)
+    _check(Cr, A, Br, "fp8", "row", "f32", sa, sb)
 
 
 @pytest.mark.parametrize("M", [1, 5, 16])

@@ -14,8 +14,6 @@ extern "C" tg_status tg_gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A,
         return st;
     if (!isfinite(scale_a) || !isfinite(scale_b))
         return TG_ERR_INVALID_VALUE;
-    if (b_layout != TG_COL_MAJOR)
-        return TG_ERR_NOT_SUPPORTED;
     tg::TileArgs a{};
     a.M = M;
     a.N = N;
@@ -27,5 +25,9 @@ extern "C" tg_status tg_gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A,
     a.C = C;
     a.ldc = ldc;
     a.alpha = scale_a * scale_b;
-    return tg::launch_dense<tg::E_FP8, tg::B_KCONTIG>(a, c_dtype, (hipStream_t)stream);
+    // a row-major B (N-contiguous) goes to the generic tile kernel, which
+    // transposes it on its way into LDS; the NT kernel takes the K-contiguous one
+    if (b_layout == TG_COL_MAJOR)
+        return tg::launch_dense<tg::E_FP8, tg::B_KCONTIG>(a, c_dtype, (hipStream_t)stream);
+    return tg::launch_dense<tg::E_FP8, tg::B_NCONTIG>(a, c_dtype, (hipStream_t)stream);
 }
