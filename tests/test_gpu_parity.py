@@ -231,6 +231,34 @@ def test_medium_multi_tile(tg, dt, lay):
         _check(C, A, B, dt, lay, "f32", sa, sb, rows=rows)
 
 
+def _random_cases(n=30, seed=2024):
+    """Seeded random problems across every dense entry point, layout and
+    output type: M often within the skinny range, K and N often off the 8- and
+    16-element grids (the generic kernel), sizes up to a few tiles."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dt = ["f16", "bf16", "fp8"][i % 3]
+        lay = ["col", "row"][(i // 3) % 2]
+        out = ["f32", "f16", "bf16"][(i // 6) % 3]
+        M = int(rng.integers(1, 17)) if rng.random() < 0.4 else int(rng.integers(17, 700))
+        N = int(rng.integers(1, 700))
+        K = int(rng.integers(1, 600))
+        if rng.random() < 0.5:  # on the 16-element grid: the fast kernels
+            K = max(16, K // 16 * 16)
+            N = max(16, N // 16 * 16)
+        cases.append((dt, lay, out, M, N, K))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: "-".join(map(str, c)))
+def test_random_shapes(tg, case):
+    dt, lay, out, M, N, K = case
+    A, B, sa, sb = _inputs(dt, M, N, K, lay, seed=M * 7 + N * 3 + K)
+    C = _run_dense(tg, dt, A, B, lay, out, scale_a=sa, scale_b=sb)
+    _check(C, A, B, dt, lay, out, sa, sb)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp8"])
 @pytest.mark.parametrize("out", ["f16", "bf16"])
 def test_large_ragged_16bit_out(tg, dt, out):
