@@ -612,6 +612,43 @@ def test_sp24_small(tg, out, shape):
     assert ok, (r, idx)
 
 
+def _random_w4_sp_cases(n=16, seed=4242):
+    """Seeded random w4a16 and 2:4-sparse problems: M across the decode,
+    small-tile and tile ranges, K on each kernel's grid (128 for w4a16, 64
+    for 2:4), ragged N."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kind = ["w4", "sp"][i % 2]
+        M = int(rng.integers(1, 17)) if rng.random() < 0.4 else int(rng.integers(17, 600))
+        N = int(rng.integers(1, 600))
+        K = int(rng.integers(1, 12)) * (128 if kind == "w4" else 64)
+        zp = int(rng.integers(0, 16))
+        out = ["f32", "f16", "bf16"][int(rng.integers(0, 3))]
+        if kind == "w4":
+            out = "f16"  # the w4a16 output type
+        else:
+            zp = 0  # (no zero point in the 2:4 format)
+        cases.append((kind, M, N, K, zp, out))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_w4_sp_cases(), ids=lambda c: "-".join(map(str, c)))
+def test_random_w4a16_sp24(tg, case):
+    kind, M, N, K, zp, out = case
+    if kind == "w4":
+        A, q, s = _w4_inputs(M, N, K, seed=M + 5 * N + K)
+        C = _run_w4(tg, A, q, s, zp=zp)
+        cref, S = oracle.w4a16(A, q, s, K, zero_point=zp)
+        ok, r, idx = ochk.check(_f64(C), cref, S, K, "f16")
+    else:
+        A, v, m = _sp_inputs(M, N, K, seed=M + 5 * N + K)
+        C = _run_sp(tg, A, v, m, out)
+        cref, S = oracle.gemm_sp24(A, v, m, K)
+        ok, r, idx = ochk.check(_f64(C), cref, S, K, out)
+    assert ok, (r, idx)
+
+
 def test_sp24_one_hot_rows_read_the_weights(tg):
     """A row that is one-hot at k gives C[., n] = W[n][k] exactly: every kept value
     lands at its coded position and every other position contributes zero."""
