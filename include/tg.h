@@ -83,9 +83,10 @@ tg_status tg_gemm_bf16(int64_t M, int64_t N, int64_t K,
 /* fp8 (OCP e4m3, "e4m3fn": bias 7, max 448, no inf) x fp8 -> fp32
  * accumulate; C = (scale_a * scale_b) * (Aq . Bq), converted to c_dtype.
  * scale_a, scale_b are per-tensor dequantisation scales passed by value
- * (finite).  Both layouts of B are taken; TG_COL_MAJOR (K-contiguous) is
- * the fast one, TG_ROW_MAJOR runs a slower kernel that transposes B on its
- * way into shared memory. */
+ * (finite).  Both layouts of B are taken.  With TG_ROW_MAJOR, problems of
+ * at least a few hundred output tiles with N and K multiples of 16 run at
+ * the speed of TG_COL_MAJOR; others run a slower kernel that transposes B
+ * on its way into shared memory. */
 tg_status tg_gemm_fp8(int64_t M, int64_t N, int64_t K,
                       const void *A, int64_t lda,
                       const void *B, int64_t ldb, tg_layout b_layout,

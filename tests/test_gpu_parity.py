@@ -126,6 +126,25 @@ def test_fp8_small(tg, lay, out, shape):
     _check(C, A, B, "fp8", lay, out, sa, sb)
 
 
+@pytest.mark.parametrize("shape", [(1280, 1296, 1040), (3600, 3408, 272), (2048, 2048, 2048)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_fp8_row_major_b_nt_path(tg, out, shape):
+    """fp8 with B row-major at sizes that pick the 128 and 256 tiles (N and K
+    multiples of 16: the NT kernel with transposing fragment reads), ragged
+    tiles and a K tail included.  The same product with B column-major runs
+    the same MFMA sequence on the same fragments: the two outputs must agree
+    bit for bit, and both meet the bound."""
+    M, N, K = shape
+    A, Bc, sa, sb = _inputs("fp8", M, N, K, "col", seed=M + N + K)
+    Br = Bc.t().contiguous()
+    Cc = _run_dense(tg, "fp8", A, Bc, "col", out, scale_a=sa, scale_b=sb)
+    Cr = _run_dense(tg, "fp8", A, Br, "row", out, scale_a=sa, scale_b=sb)
+    assert torch.equal(Cc, Cr)
+    rows = np.r_[0:24, M // 2 : M // 2 + 24, M - 24 : M]
+    _check(Cr, A, Br, "fp8", "row", out, sa, sb, rows=rows)
+
+
 def test_fp8_row_major_b_matches_col(tg):
     """The same fp8 product with B stored row-major and column-major: both
     within the bound, and the oracle's two layouts give one reference."""

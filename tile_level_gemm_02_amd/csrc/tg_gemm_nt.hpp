@@ -27,9 +27,10 @@
 //    hide its skew and the first reads of the next step;
 //  * epilogue: scale (fp8), round to the output type, staged through LDS so
 //    that every store instruction writes whole 128-byte lines;
-//  * a row-major (N-contiguous) 16-bit B is taken too (BL = B_NCONTIG): its
+//  * a row-major (N-contiguous) B is taken too (BL = B_NCONTIG): its
 //    half-stage holds the step's k rows of the tile's columns, and each B
-//    fragment comes from transposing LDS reads (ds_read_b64_tr_b16).
+//    fragment comes from transposing LDS reads (ds_read_b64_tr_b16 for
+//    16-bit elements, ds_read_b64_tr_b8 for fp8).
 #pragma once
 
 #include <type_traits>
@@ -122,18 +123,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     // bytes), copied RPIN rows per instruction and read by the transposing
     // LDS load (16-bit elements only)
     constexpr bool NB = BL == B_NCONTIG;
-    static_assert(!NB || EB == 2, "N-contiguous B: 16-bit elements");
     constexpr int RBN = BN * EB, CHN = RBN / 16, RPIN = 1024 / RBN;
     static_assert(!NB || (KE * RBN == HALF && CHN >= 8 && (KE / RPIN) % NW == 0 && KE / RPIN / NW == BI),
                   "N-contiguous B stage: same size and copy count as the K-contiguous one");
-    // physical chunk of logical chunk c of B row k is c ^ swn(k): the four
-    // rows k .. k+3 that one transposing read takes (32 bytes each, two
-    // 16-lane groups side by side) fall in distinct banks
+    // physical chunk of logical chunk c of B row k is c ^ swn(k).  16-bit:
+    // the four rows k .. k+3 that one transposing read takes (32 bytes each,
+    // two 16-lane groups side by side) fall in distinct banks.  8-bit: a
+    // transposing read takes 16 bytes of each of 8 rows k .. k+7 per 16-lane
+    // group (two groups side by side in one chunk pair, two more 32 rows
+    // further down); rows k .. k+7 spread over 8 chunk positions and rows
+    // 32 apart over the other 8, so the 512 bytes meet each bank twice.
     auto swn = [](uint32_t k) __attribute__((always_inline)) -> uint32_t {
-        if constexpr (CHN >= 16)
+        if constexpr (EB == 1) {
+            if constexpr (CHN >= 16)
+                return (k % 8u) | (8u * ((k / 32u) % 2u));
+            else
+                return ((k / 2u) % 4u) | (4u * ((k / 32u) % 2u));  // 128-byte rows: two rows per bank line
+        } else if constexpr (CHN >= 16) {
             return 4u * (k % 4u);
-        else
+        } else {
             return 4u * ((((k % 4u) + 1u) / 2u) % 2u);  // 128-byte rows: two rows per bank line
+        }
     };
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[NH * HALF];
@@ -267,7 +277,34 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         const uint8_t* st = is_a ? a_ptr(kt) : b_ptr(kt);
         const uint32_t row0 = (is_a ? a_row0 : b_row0) + (uint32_t)idx * 32 * RB;
         Frag f;
-        if constexpr (NB) {
+        if constexpr (NB && EB == 1) {
+            if (!is_a) {
+                // 32 k of column n of the block from four transposing reads (8
+                // k each): in each 16-lane group, source lane 2e + a addresses
+                // k row (base + e), columns 8a .. 8a+7 of the group's 16, and
+                // lane 8a + j receives column 8a + j at rows base .. base+7
+                const uint32_t l16 = lane % 16u;
+                const uint32_t col = wn * (BN / WN) + (uint32_t)idx * 32u + 16u * ((lane / 16u) % 2u) + 8u * (l16 % 2u);
+                // rows k0 + 8*r2 share swn(k0) (same k % 8, same 32-row block):
+                // one address, the four reads 8 rows apart
+                const uint32_t k0 = (uint32_t)(64 * s) + 32u * lgrp + l16 / 2u;
+                const uint32_t off = k0 * RBN + (((col / CE) ^ swn(k0)) << 4) + (col % CE);
+                uint32_t w[8];
+#pragma unroll
+                for (int r2 = 0; r2 < 4; ++r2) {
+                    const v2i32_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) v2i32_t*)(lds_u8_t)(st + off + (uint32_t)r2 * 8u * RBN));
+                    w[2 * r2] = (uint32_t)v[0];
+                    w[2 * r2 + 1] = (uint32_t)v[1];
+                }
+                f = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+            } else {
+                const uint32_t c0 = (uint32_t)(4 * s) + 2u * lgrp;
+                const u32x4 lo = lds128(st, row0 + ((c0 ^ sw) << 4));
+                const u32x4 hi = lds128(st, row0 + (((c0 + 1u) ^ sw) << 4));
+                f = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+        } else if constexpr (NB) {
             if (!is_a) {
                 // 8 k of column n of the block from two transposing reads (4 k
                 // each): in each 16-lane group, source lane 4e + a addresses k

@@ -106,18 +106,20 @@ inline bool nt_eligible(const TileArgs& a)
     return (a.K % (16 / EB)) == 0 && 256 * a.lda * EB + a.K * EB < lim && 256 * a.ldb * EB + a.K * EB < lim;
 }
 
-// The NT kernel with an N-contiguous (row-major) B: 16-bit elements, whole
-// 16-byte chunks along K for A and along N for B, and 32-bit buffer offsets
-// over the K rows of B (plus the rows of the steps past K that the ring forms).
+// The NT kernel with an N-contiguous (row-major) B: whole 16-byte chunks
+// along K for A and along N for B, and 32-bit buffer offsets over the K rows
+// of B (plus the rows of the steps past K that the ring forms).  8-bit B rows
+// of a 64-wide tile would be 64 bytes, too narrow for its staging: fp8 takes
+// this path only where the 128 or 256 tile is picked.
 template <int E>
 inline bool nt_eligible_nrow(const TileArgs& a)
 {
-    constexpr int EB = ElemInfo<E>::bytes;
-    if constexpr (EB != 2)
-        return false;
+    constexpr int EB = ElemInfo<E>::bytes, CE = 16 / EB, KE = 128 / EB;
     const int64_t lim = (int64_t)kNumRecords;
-    return (a.K % 8) == 0 && (a.N % 8) == 0 && 256 * a.lda * EB + a.K * EB < lim &&
-           (a.K + 6 * 64) * a.ldb * EB + 256 * EB < lim;
+    if (EB == 1 && pick_tile(a.M, a.N, true) < 128)
+        return false;
+    return (a.K % CE) == 0 && (a.N % CE) == 0 && 256 * a.lda * EB + a.K * EB < lim &&
+           (a.K + 6 * KE) * a.ldb * EB + 256 * EB < lim;
 }
 
 // Staging of the NT kernel: bytes of K per staged row, and LDS half-stages in
@@ -150,11 +152,15 @@ template <int E, int O, int BL = B_KCONTIG>
 tg_status launch_nt_sized(TileArgs& a, hipStream_t s)
 {
     a.group_m = 4;
-    switch (pick_tile(a.M, a.N, true)) {
-    case 256: return launch_nt<E, O, 256, 256, BL>(a, s);
-    case 128: return launch_nt<E, O, 128, 128, BL>(a, s);
-    default: return launch_nt<E, O, 64, 64, BL>(a, s);
-    }
+    const int t = pick_tile(a.M, a.N, true);
+    if (t == 256)
+        return launch_nt<E, O, 256, 256, BL>(a, s);
+    if constexpr (ElemInfo<E>::bytes == 1 && BL == B_NCONTIG)
+        return launch_nt<E, O, 128, 128, BL>(a, s);  // (nt_eligible_nrow has ruled out the 64 tile)
+    else if (t == 128)
+        return launch_nt<E, O, 128, 128, BL>(a, s);
+    else
+        return launch_nt<E, O, 64, 64, BL>(a, s);
 }
 
 template <int E, int BL>
@@ -168,7 +174,7 @@ tg_status launch_dense(TileArgs& a, int c_dtype, hipStream_t s)
             default: return launch_nt_sized<E, O_BF16>(a, s);
             }
         }
-    } else if constexpr (ElemInfo<E>::bytes == 2) {
+    } else {
         if (nt_eligible_nrow<E>(a)) {
             switch (c_dtype) {
             case TG_F32: return launch_nt_sized<E, O_F32, B_NCONTIG>(a, s);
