@@ -453,6 +453,21 @@ def test_w4a16_decode(tg, shape, zp):
 
 # the decode kernel with row strides above the minimum on every operand
 # (odd scale stride, scales only 2-byte aligned) and K == 0 (zeros stored)
+# Batches of 17 .. 48 rows: the decode kernel in 16-row slices (one
+# workgroup per column block and slice; column blocks padded to a multiple
+# of 8 when there are several slices), K a multiple of 1024; 64 rows: the
+# tile kernel again
+@pytest.mark.parametrize("shape", [(17, 200, 1024), (31, 264, 2048), (32, 1000, 1024), (33, 96, 3072),
+                                   (48, 2048, 4096), (64, 520, 1024)], ids=lambda s: "x".join(map(str, s)))
+def test_w4a16_decode_row_slices(tg, shape):
+    M, N, K = shape
+    A, q, s = _w4_inputs(M, N, K, seed=M + 3 * N)
+    C = _run_w4(tg, A, q, s, zp=5)
+    cref, S = oracle.w4a16(A, q, s, K, zero_point=5)
+    ok, r, idx = ochk.check(_f64(C), cref, S, K, "f16")
+    assert ok, (r, idx)
+
+
 def test_w4a16_decode_layouts_and_k0(tg):
     M, N, K = 11, 72, 640
     A, q, s = _w4_inputs(M, N, K, seed=43)

@@ -445,7 +445,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4(TileArgs p)
 }
 
 // --------------------------------------------------------------------------
-// The decode kernel with every operand copied to LDS (w4a16, M <= 16, K a
+// The decode kernel with every operand copied to LDS (w4a16, 16 rows per
+// workgroup: batches of more rows run one workgroup per 16-row slice; K a
 // multiple of 1024, scales 4-byte aligned with an even stride).  The cost of
 // skinny_w4 is the texture-address work of its load instructions, not their
 // bytes: each 64-lane load takes the same address-unit time whether its
@@ -483,15 +484,25 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t n0 = (int64_t)blockIdx.x * COLS;
+    const int64_t N = p.N, K = p.K;
+    // Rows come in slices of 16 (one per workgroup): workgroup id -> (column
+    // block, slice) so that the S slices of a column block have ids 8 apart,
+    // i.e. run on one XCD at about the same time and share its L2's copy of
+    // the block's weights.  With S = 1 this is the identity.
+    const int64_t S = (p.M + 15) / 16;
+    const int64_t grp8 = (int64_t)blockIdx.x / (8 * S), rem = (int64_t)blockIdx.x % (8 * S);
+    const int64_t slice = rem / 8, cb = grp8 * 8 + rem % 8;
+    const int64_t n0 = cb * COLS;
+    if (n0 >= N)
+        return;  // padding of the last group of eight column blocks (whole workgroup)
+    const int64_t M = p.M - 16 * slice < 16 ? p.M - 16 * slice : 16;  // rows of this slice
     const int64_t KG = K / 128;  // a multiple of 2*WAVES: every wave gets whole stages
     const int64_t g0 = KG * wave / WAVES, nst = KG / (2 * WAVES);
     uint8_t* ring = lds + wave * (RING * SLOT);
     if (tid == 0)
         *(u32x4*)(lds + ZERO) = u32x4{0u, 0u, 0u, 0u};
 
-    const i32x4_t ra = make_rsrc(p.A);
+    const i32x4_t ra = make_rsrc(p.A + 16 * slice * p.lda * 2);
     const i32x4_t rq = make_rsrc(p.qw + n0 * p.ldq);
     const i32x4_t rs = make_rsrc(p.scales + n0 * p.lds);
     // copy lanes: words -- instruction i, column 8i + lane/8, physical chunk
@@ -597,7 +608,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
     __syncthreads();
     for (int t = (int)wave; t < NT; t += WAVES) {  // wave t sums tile t over the K split, in wave order
         const int64_t col = n0 + 16 * t + c;
-        uint16_t* C = (uint16_t*)p.C;
+        uint16_t* C = (uint16_t*)p.C + 16 * slice * p.ldc;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             float sum = red[(t * 4 + v) * 64 + lane];
