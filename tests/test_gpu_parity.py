@@ -188,6 +188,22 @@ def test_skinny_outputs_strided(tg, out, M, K):
 # when N and K are multiples of 8: ragged tiles on every side, K tails of one
 # chunk and of several, padded leading dimensions, all outputs; and a large
 # case on sampled rows.
+# Batches of 17 .. 64 rows against a K-contiguous B: the skinny kernel in
+# 16-row slices (column blocks padded to a multiple of 8 when there are
+# several slices), ragged N, K tails, and narrow N with fp32 output (the
+# slices split K over workgroups too)
+@pytest.mark.parametrize("shape", [(17, 200, 1000), (24, 1000, 4096), (32, 264, 4101), (33, 520, 136),
+                                   (48, 2056, 2048), (64, 88, 520), (64, 1024, 8192)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_skinny_row_slices(tg, dt, out, shape):
+    M, N, K = shape
+    A, B, _, _ = _inputs(dt, M, N, K, "col", seed=M + 2 * N + K)
+    C = _run_dense(tg, dt, A, B, "col", out)
+    _check(C, A, B, dt, "col", out)
+
+
 @pytest.mark.parametrize("shape", [(300, 264, 200), (1000, 1288, 1032), (257, 520, 72), (64, 8, 8),
                                    (513, 1024, 4104)], ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])

@@ -1,5 +1,6 @@
 // The GEMM for M <= 16 rows against a K-contiguous B (decode-shaped products:
-// a few activation rows against a weight stored N x K).  Streaming B from
+// a few activation rows against a weight stored N x K); batches of a few
+// times 16 rows run one workgroup per 16-row slice.  Streaming B from
 // HBM is the whole cost.  The waves of a workgroup split K and reduce their
 // partial tiles through LDS -- the intra-block split-K of the TileScale
 // README's GEMM example (section "Example of GEMM"), where warpgroups split
@@ -65,8 +66,19 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t n0 = (int64_t)blockIdx.x * kSkCols;
+    const int64_t N = p.N, K = p.K;
+    // Rows come in slices of 16 (one per workgroup): workgroup id -> (column
+    // block, slice) so that the S slices of a column block have ids 8 apart,
+    // i.e. run on one XCD at about the same time and share its L2's copy of
+    // the block's B rows.  With S = 1 this is the identity.
+    const int64_t S = (p.M + 15) / 16;
+    const int64_t grp8 = (int64_t)blockIdx.x / (8 * S), rem = (int64_t)blockIdx.x % (8 * S);
+    const int64_t slice = rem / 8;
+    const int64_t n0 = (grp8 * 8 + rem % 8) * kSkCols;
+    if (n0 >= N)
+        return;  // padding of the last group of eight column blocks (whole workgroup)
+    const int64_t M = p.M - 16 * slice < 16 ? p.M - 16 * slice : 16;  // rows of this slice
+    const uint8_t* const Ab = p.A + 16 * slice * p.lda * 2;
     const int64_t KS = K / kSkKE;  // whole stages
     // this workgroup's stages [z0, z1), split over its waves in contiguous ranges
     const int64_t z0 = SPLIT ? KS * blockIdx.y / gridDim.y : 0;
@@ -81,7 +93,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
     // past M or N and stages past the wave's range read through an
     // out-of-range offset (zeros).  The host guarantees every valid offset,
     // plus the stage offsets the ring forms, stays below 2^31.
-    const i32x4_t ra = make_rsrc(p.A);
+    const i32x4_t ra = make_rsrc(Ab);
     const i32x4_t rb = make_rsrc(p.B + n0 * p.ldb * 2);
     uint32_t vb[2], va[AI];
 #pragma unroll
@@ -147,7 +159,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
             const int64_t k = kb * 32 + h * 8;
             u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
             if ((int64_t)c16 < M && k < K) {
-                const uint8_t* src = p.A + ((int64_t)c16 * p.lda + k) * 2;
+                const uint8_t* src = Ab + ((int64_t)c16 * p.lda + k) * 2;
                 a = (k + 8 <= K) ? ldg128(src) : load_chunk_partial<2>(src, K - k);
             }
             if (n0 + c16 < N && k < K) {
@@ -167,7 +179,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
         red[(wave * 4 + v) * 64 + lane] = acc[0][v] + acc[1][v];
     __syncthreads();
     if (wave == 0) {  // sum over the K split, in wave order
-        OutT* C = (OutT*)p.C;
+        OutT* C = (OutT*)p.C + 16 * slice * p.ldc;
         const int64_t r = c16;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -178,7 +190,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
             const int64_t col = n0 + 4 * h + v;
             if (r < M && col < N) {
                 if constexpr (SPLIT)
-                    atomicAdd((float*)p.C + r * p.ldc + col, sum);
+                    atomicAdd((float*)C + r * p.ldc + col, sum);
                 else
                     C[r * p.ldc + col] = convert_out<O>(sum);
             }
