@@ -136,16 +136,31 @@ template <> struct NtRing<E_FP8, 256> { static constexpr int NH = 5; };
 template <int BM, int BN> struct NtWaves { static constexpr int WM = 2, WN = 2; };
 template <> struct NtWaves<256, 256> { static constexpr int WM = 2, WN = 4; };
 
-template <int E, int O, int BM, int BN, int BL = B_KCONTIG>
+template <int E, int O, int BM, int BN, int BL = B_KCONTIG, int NH = NtRing<E, BM>::NH>
 tg_status launch_nt(const TileArgs& a, hipStream_t s)
 {
     const int64_t tiles = n_tiles<BM, BN>(a.M, a.N);
     if (tiles > 0x7FFFFFFF)
         return TG_ERR_NOT_SUPPORTED;
-    constexpr int RB = NtStaging<E>::RB, NH = NtRing<E, BM>::NH;
+    constexpr int RB = NtStaging<E>::RB;
     constexpr int WM = NtWaves<BM, BN>::WM, WN = NtWaves<BM, BN>::WN;
     hipLaunchKernelGGL((gemm_nt<E, O, BM, BN, RB, NH, WM, WN, BL>), dim3((uint32_t)tiles), dim3(64 * WM * WN), 0, s, a);
     return launched();
+}
+
+// The 128 and 64 tiles: a ring of 8 half-stages (4 steps in flight) when the
+// tiles fit the chip at the occupancy that allows (one 128 KiB workgroup, or
+// two of 64 KiB, per CU); else 4, which leaves room for more resident
+// workgroups.  A small tile does little MFMA work per K step, so with 2 steps
+// in flight it waits on copy latency: at N = K = 8192, M = 128 (64 tiles)
+// 96 -> 45 us, M = 256 (128 tiles) 114 -> 77 us; 2048^3 27 -> 21 us.
+template <int E, int O, int BM, int BL>
+tg_status launch_nt_ring(const TileArgs& a, hipStream_t s)
+{
+    const int64_t per_round = BM == 128 ? 256 : 512;
+    if (n_tiles<BM, BM>(a.M, a.N) <= per_round)
+        return launch_nt<E, O, BM, BM, BL, 8>(a, s);
+    return launch_nt<E, O, BM, BM, BL, 4>(a, s);
 }
 
 template <int E, int O, int BL = B_KCONTIG>
@@ -156,11 +171,11 @@ tg_status launch_nt_sized(TileArgs& a, hipStream_t s)
     if (t == 256)
         return launch_nt<E, O, 256, 256, BL>(a, s);
     if constexpr (ElemInfo<E>::bytes == 1 && BL == B_NCONTIG)
-        return launch_nt<E, O, 128, 128, BL>(a, s);  // (nt_eligible_nrow has ruled out the 64 tile)
+        return launch_nt_ring<E, O, 128, BL>(a, s);  // (nt_eligible_nrow has ruled out the 64 tile)
     else if (t == 128)
-        return launch_nt<E, O, 128, 128, BL>(a, s);
+        return launch_nt_ring<E, O, 128, BL>(a, s);
     else
-        return launch_nt<E, O, 64, 64, BL>(a, s);
+        return launch_nt_ring<E, O, 64, BL>(a, s);
 }
 
 template <int E, int BL>
