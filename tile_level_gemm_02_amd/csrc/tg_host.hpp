@@ -243,9 +243,9 @@ void launch_skinny(const SkinnyArgs& sa, int64_t blocks, int split, hipStream_t 
 
 // Batches up to this many rows against a K-contiguous B take the skinny
 // kernel, in 16-row slices (each slice re-reads B, mostly from L2).  At
-// N = K = 8192 (bf16): 17 rows 36 us against 102 for the tile kernel, 32
-// rows 42 against 103, 64 rows 67 against 97; 96 rows would not gain.
-constexpr int64_t kSkSliceMaxM = 64;
+// N = K = 8192 (bf16, flushed): 17 rows 37 us and 32 rows 43 against 46 for
+// the 64-tile NT kernel; from 40 rows on (53 us) the tile kernel is faster.
+constexpr int64_t kSkSliceMaxM = 32;
 
 // fp16 / bf16 GEMM.  Few rows (kSkSliceMaxM) against a K-contiguous B take
 // the skinny kernel; everything else the tile kernel (K == 0 runs it with no
