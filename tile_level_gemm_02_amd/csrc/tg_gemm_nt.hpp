@@ -128,17 +128,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
                   "N-contiguous B stage: same size and copy count as the K-contiguous one");
     // physical chunk of logical chunk c of B row k is c ^ swn(k).  16-bit:
     // the four rows k .. k+3 that one transposing read takes (32 bytes each,
-    // two 16-lane groups side by side) fall in distinct banks.  8-bit: a
-    // transposing read takes 16 bytes of each of 8 rows k .. k+7 per 16-lane
-    // group (two groups side by side in one chunk pair, two more 32 rows
-    // further down); rows k .. k+7 spread over 8 chunk positions and rows
-    // 32 apart over the other 8, so the 512 bytes meet each bank twice.
+    // two 16-lane groups side by side) fall in distinct banks.  8-bit: each
+    // half-wave of a transposing read takes 16 bytes of each of 8 rows
+    // k .. k+7 in logical chunk c (c even) and 8 more in chunk c ^ 1; with
+    // swn even, rows k .. k+7 of chunk c land on the 8 even chunk positions
+    // and those of chunk c ^ 1 on the 8 odd ones: 256 bytes, every bank once.
     auto swn = [](uint32_t k) __attribute__((always_inline)) -> uint32_t {
         if constexpr (EB == 1) {
             if constexpr (CHN >= 16)
-                return (k % 8u) | (8u * ((k / 32u) % 2u));
+                return 2u * (k % 8u);
             else
-                return ((k / 2u) % 4u) | (4u * ((k / 32u) % 2u));  // 128-byte rows: two rows per bank line
+                return 2u * ((k / 2u) % 4u);  // 128-byte rows: two rows per bank line
         } else if constexpr (CHN >= 16) {
             return 4u * (k % 4u);
         } else {
@@ -285,8 +285,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
                 // lane 8a + j receives column 8a + j at rows base .. base+7
                 const uint32_t l16 = lane % 16u;
                 const uint32_t col = wn * (BN / WN) + (uint32_t)idx * 32u + 16u * ((lane / 16u) % 2u) + 8u * (l16 % 2u);
-                // rows k0 + 8*r2 share swn(k0) (same k % 8, same 32-row block):
-                // one address, the four reads 8 rows apart
+                // rows k0 + 8*r2 share swn(k0) (same k % 8): one address, the
+                // four reads 8 rows apart
                 const uint32_t k0 = (uint32_t)(64 * s) + 32u * lgrp + l16 / 2u;
                 const uint32_t off = k0 * RBN + (((col / CE) ^ swn(k0)) << 4) + (col % CE);
                 uint32_t w[8];
