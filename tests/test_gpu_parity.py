@@ -294,6 +294,20 @@ def test_random_shapes(tg, case):
     _check(C, A, B, dt, lay, out, sa, sb)
 
 
+# The 128 tile takes an 8-deep LDS ring up to 256 tiles and a 4-deep one
+# above (2048 x 2048: 256 tiles; 2048 x 2176: 272); the 64 tile always the
+# deep one (1024 x 1008: 256 tiles of 64)
+@pytest.mark.parametrize("shape", [(2048, 2048, 528), (2048, 2176, 528), (1024, 1008, 272)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dt,lay", [("bf16", "col"), ("f16", "row"), ("fp8", "col")])
+def test_ring_depth_boundary(tg, dt, lay, shape):
+    M, N, K = shape
+    A, B, sa, sb = _inputs(dt, M, N, K, lay, seed=M + N + K)
+    C = _run_dense(tg, dt, A, B, lay, "f32", scale_a=sa, scale_b=sb)
+    rows = np.r_[0:16, M // 2 : M // 2 + 16, M - 16 : M]
+    _check(C, A, B, dt, lay, "f32", sa, sb, rows=rows)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp8"])
 @pytest.mark.parametrize("out", ["f16", "bf16"])
 def test_large_ragged_16bit_out(tg, dt, out):

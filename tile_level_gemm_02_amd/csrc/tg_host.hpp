@@ -154,13 +154,18 @@ tg_status launch_nt(const TileArgs& a, hipStream_t s)
 // workgroups.  A small tile does little MFMA work per K step, so with 2 steps
 // in flight it waits on copy latency: at N = K = 8192, M = 128 (64 tiles)
 // 96 -> 45 us, M = 256 (128 tiles) 114 -> 77 us; 2048^3 27 -> 21 us.
+// (pick_tile takes the 64 tile only below 96 tiles of 128, i.e. for at
+// most 384 tiles of 64: always the deep ring.)
 template <int E, int O, int BM, int BL>
 tg_status launch_nt_ring(const TileArgs& a, hipStream_t s)
 {
-    const int64_t per_round = BM == 128 ? 256 : 512;
-    if (n_tiles<BM, BM>(a.M, a.N) <= per_round)
-        return launch_nt<E, O, BM, BM, BL, 8>(a, s);
-    return launch_nt<E, O, BM, BM, BL, 4>(a, s);
+    if constexpr (BM == 64) {
+        return launch_nt<E, O, 64, 64, BL, 8>(a, s);
+    } else {
+        if (n_tiles<BM, BM>(a.M, a.N) <= 256)
+            return launch_nt<E, O, BM, BM, BL, 8>(a, s);
+        return launch_nt<E, O, BM, BM, BL, 4>(a, s);
+    }
 }
 
 template <int E, int O, int BL = B_KCONTIG>
