@@ -155,3 +155,29 @@ def test_product_and_oracle_share_no_code():
             assert not re.search(r"^\s*(import|from)\s+tile_level_gemm_02_amd\b", text, re.M), f
             assert not re.search(r"#\s*include\s*[<\"].*tg(_\w+)?\.h", text), f
             assert "libtg" not in text, f
+
+
+def test_package_imports_without_the_library(tmp_path):
+    """A checkout with no libtg.so built: the package and its build module
+    import (so the library can be built from it), and the first entry-point
+    call raises ImportError -- there is no fallback."""
+    import shutil
+    import subprocess
+    import sys
+
+    pkg = os.path.join(ROOT, "tile_level_gemm_02_amd")
+    dst = tmp_path / "tile_level_gemm_02_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    assert not (dst / "libtg.so").exists()
+    code = (
+        "import tile_level_gemm_02_amd.build as b, tile_level_gemm_02_amd as t\n"
+        "assert callable(b.build)\n"
+        "try:\n"
+        "    t.tg_version()\n"
+        "except ImportError as e:\n"
+        "    print('raised', 'not built' in str(e))\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], cwd=str(tmp_path), capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "raised True", r.stdout

@@ -2,8 +2,11 @@
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/tg.h.  torch supplies device
-memory and the current HIP stream.  There is no fallback: if libtg.so is
-missing or fails to load, importing this package raises.
+memory and the current HIP stream.  There is no fallback: libtg.so is loaded
+on the first call of any entry point (or of ``load()``), and if it is missing
+or fails to load that call raises ImportError.  Importing the package loads
+nothing, so its build module (``python -m tile_level_gemm_02_amd.build``)
+runs in a checkout where the library is not built yet.
 
 Entry points (same names as the C ABI):
 
@@ -58,7 +61,8 @@ def _load() -> ctypes.CDLL:
     lib.tg_gemm_w4a16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, i32, vp, i64, vp]
     lib.tg_dequant_w4.argtypes = [i64, i64, vp, i64, vp, i64, i32, i32, vp, i64, vp]
     lib.tg_gemm_sp24_bf16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, vp]
-    for name in ("tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16", "tg_dequant_w4"):
+    for name in ("tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16", "tg_dequant_w4",
+                 "tg_gemm_sp24_bf16"):
         getattr(lib, name).restype = ci
     lib.tg_status_string.argtypes = [ci]
     lib.tg_status_string.restype = ctypes.c_char_p
@@ -67,15 +71,30 @@ def _load() -> ctypes.CDLL:
     return lib
 
 
-lib = _load()
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """The loaded libtg.so (loaded on first use; raises ImportError if it is not built)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def __getattr__(name: str):
+    # ``tile_level_gemm_02_amd.lib`` is the loaded library, resolved on first access
+    if name == "lib":
+        return load()
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")
 
 
 def tg_status_string(code: int) -> str:
-    return lib.tg_status_string(int(code)).decode()
+    return load().tg_status_string(int(code)).decode()
 
 
 def tg_version() -> int:
-    return int(lib.tg_version())
+    return int(load().tg_version())
 
 
 # ------------------------------------------------------------- marshalling
@@ -130,14 +149,14 @@ def tg_gemm_f16(A, B, C, b_layout: str = "row", stream=None) -> None:
     """C = A.B with fp16 A, B (fp32 accumulate); see include/tg.h."""
     if A.dtype != torch.float16 or B.dtype != torch.float16:
         raise ValueError("tg_gemm_f16 takes float16 A and B")
-    _ok("tg_gemm_f16", lib.tg_gemm_f16(*_dense("tg_gemm_f16", A, B, C, b_layout, stream)))
+    _ok("tg_gemm_f16", load().tg_gemm_f16(*_dense("tg_gemm_f16", A, B, C, b_layout, stream)))
 
 
 def tg_gemm_bf16(A, B, C, b_layout: str = "row", stream=None) -> None:
     """C = A.B with bf16 A, B (fp32 accumulate); see include/tg.h."""
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise ValueError("tg_gemm_bf16 takes bfloat16 A and B")
-    _ok("tg_gemm_bf16", lib.tg_gemm_bf16(*_dense("tg_gemm_bf16", A, B, C, b_layout, stream)))
+    _ok("tg_gemm_bf16", load().tg_gemm_bf16(*_dense("tg_gemm_bf16", A, B, C, b_layout, stream)))
 
 
 def tg_gemm_sp24_bf16(A, Wv, Wm, C, stream=None) -> None:
@@ -153,7 +172,7 @@ def tg_gemm_sp24_bf16(A, Wv, Wm, C, stream=None) -> None:
         raise ValueError("inconsistent sparse GEMM shapes")
     if C.dtype not in _CDTYPE:
         raise ValueError(f"unsupported C dtype {C.dtype}")
-    _ok("tg_gemm_sp24_bf16", lib.tg_gemm_sp24_bf16(M, N, K, pa, lda, pv, ldv, pm, ldm, pc, ldc,
+    _ok("tg_gemm_sp24_bf16", load().tg_gemm_sp24_bf16(M, N, K, pa, lda, pv, ldv, pm, ldm, pc, ldc,
                                                    _CDTYPE[C.dtype], _stream(stream)))
 
 
@@ -162,7 +181,7 @@ def tg_gemm_fp8(A, B, C, scale_a: float, scale_b: float, b_layout: str = "col", 
     if A.dtype != torch.float8_e4m3fn or B.dtype != torch.float8_e4m3fn:
         raise ValueError("tg_gemm_fp8 takes float8_e4m3fn A and B")
     M, N, K, pa, lda, pb, ldb, lay, pc, ldc, cd, st = _dense("tg_gemm_fp8", A, B, C, b_layout, stream)
-    _ok("tg_gemm_fp8", lib.tg_gemm_fp8(M, N, K, pa, lda, pb, ldb, lay, float(scale_a), float(scale_b),
+    _ok("tg_gemm_fp8", load().tg_gemm_fp8(M, N, K, pa, lda, pb, ldb, lay, float(scale_a), float(scale_b),
                                        pc, ldc, cd, st))
 
 
@@ -178,7 +197,7 @@ def tg_gemm_w4a16(A, qweight, scales, C, group_size: int = 128, zero_point: int 
     Mc, Nc, ldc, pc = _mat(C, "C")
     if Ns != N or (Mc, Nc) != (M, N):
         raise ValueError("inconsistent w4a16 shapes")
-    _ok("tg_gemm_w4a16", lib.tg_gemm_w4a16(M, N, K, pa, lda, pq, ldq, ps, lds, int(group_size),
+    _ok("tg_gemm_w4a16", load().tg_gemm_w4a16(M, N, K, pa, lda, pq, ldq, ps, lds, int(group_size),
                                            int(zero_point), pc, ldc, _stream(stream)))
 
 
@@ -193,5 +212,5 @@ def tg_dequant_w4(qweight, scales, W, K: int | None = None, group_size: int = 12
     K = Kw if K is None else K
     if Ns != N or Nw != N or Kw != K:
         raise ValueError("inconsistent dequant shapes")
-    _ok("tg_dequant_w4", lib.tg_dequant_w4(N, K, pq, ldq, ps, lds, int(group_size), int(zero_point),
+    _ok("tg_dequant_w4", load().tg_dequant_w4(N, K, pq, ldq, ps, lds, int(group_size), int(zero_point),
                                            pw, ldw, _stream(stream)))
