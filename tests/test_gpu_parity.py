@@ -1,11 +1,13 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Acceptance per element (the bound in oracle/check.py):
+Acceptance per element (the bound in oracle/check.py), for every dtype,
+fp8 included:
     |C_gpu - C_ref| <= 2*K*2^-24*S + one output ulp,     S = sum |a||b|
-bit-exact for the int4 dequant and for inputs whose exact result is
-representable (identity, all-ones).  Small shapes span several tiles with
-ragged tails on every side; the full workload sizes are checked on sampled
-rows that the oracle computes in full.
+bit-exact for the int4 dequant (also inside every w4a16 GEMM kernel) and
+for inputs whose exact result is representable (identity, permutation,
+one-hot, all-ones) on every production kernel.  Small shapes span several
+tiles with ragged tails on every side; the full workload sizes are compared
+on every output element.
 """
 import numpy as np
 import pytest
@@ -74,17 +76,42 @@ def _inputs(dt, M, N, K, lay, seed):
     return A, B, 1.0, 1.0
 
 
-def _check(C, A, B, dt, lay, out, sa=1.0, sb=1.0, rows=None, inner_rel=None):
-    """Bound check; fp8 adds the inner-sum term of the fp8 matrix instruction unless told not to."""
+def _check(C, A, B, dt, lay, out, sa=1.0, sb=1.0, rows=None, inner_rel=0.0):
+    """Every element of C (or of the rows `rows`) within the bound of the oracle.
+
+    `inner_rel` widens the bound by inner_rel*S; only the fp8 cases named in
+    FP8_WIDENED pass it, and for them the ratio against the plain bound is
+    printed as well."""
     K = A.shape[1]
-    if inner_rel is None:
-        inner_rel = ochk.FP8_INNER_REL if dt == "fp8" else 0.0
     Ah = A if rows is None else A[rows]
     cref, S = oracle.gemm(FMT[dt], Ah, B, oracle.B_KN if lay == "row" else oracle.B_NK, sa, sb)
     got = _f64(C if rows is None else C[rows])
     ok, ratio, idx = ochk.check(got, cref, S, K, out, inner_rel)
+    if inner_rel:
+        _, plain, pidx = ochk.check(got, cref, S, K, out)
+        print(f"\nfp8 case with the widened bound: plain-bound ratio {plain:.3g} at {pidx}, "
+              f"widened-bound ratio {ratio:.3g}", flush=True)
     assert ok, f"max |err|/tol = {ratio:.3g} at {idx}: gpu {got[idx]!r} ref {cref[idx]!r}"
     return ratio
+
+
+# The fp8 parity cases that pass the widened bound (oracle/check.py
+# FP8_INNER_REL) instead of the plain one.  The fp8 matrix instruction sums
+# each group of 8 consecutive k by aligning the products to the largest one
+# and truncating below 2^(E-13) (test_fp8_inner_sum_model pins this on the
+# GPU); with fp32 output (no output ulp of slack) and few k per output the
+# plain bound 2*K*2^-24*S is tighter than that truncation.  Measured plain-
+# bound ratios on the GPU: 1.53 and 13.4; every other fp8 case meets the
+# plain bound (worst 0.63).
+FP8_WIDENED = {
+    (3600, 3400, 136, "f32"): "K = 136, fp32 output: 17 instruction groups per output",
+    (10, 16, 16, "f32"): "K = 16, fp32 output: 2 instruction groups per output",
+}
+
+
+def _fp8_inner(dt, M, N, K, out):
+    """FP8_INNER_REL for a named case of FP8_WIDENED, else 0 (the plain bound)."""
+    return ochk.FP8_INNER_REL if dt == "fp8" and (M, N, K, out) in FP8_WIDENED else 0.0
 
 
 SMALL = [(1, 1, 1), (7, 9, 13), (16, 40, 72), (64, 64, 64), (65, 63, 129), (130, 200, 100),
@@ -141,8 +168,7 @@ def test_fp8_row_major_b_nt_path(tg, out, shape):
     Cc = _run_dense(tg, "fp8", A, Bc, "col", out, scale_a=sa, scale_b=sb)
     Cr = _run_dense(tg, "fp8", A, Br, "row", out, scale_a=sa, scale_b=sb)
     assert torch.equal(Cc, Cr)
-    rows = np.r_[0:24, M // 2 : M // 2 + 24, M - 24 : M]
-    _check(Cr, A, Br, "fp8", "row", out, sa, sb, rows=rows)
+    _check(Cr, A, Br, "fp8", "row", out, sa, sb)
 
 
 def test_fp8_row_major_b_matches_col(tg):
@@ -212,15 +238,14 @@ def test_row_major_b_nt_path(tg, dt, out, shape):
     M, N, K = shape
     A, B, _, _ = _inputs(dt, M, N, K, "row", seed=M + 3 * N + K)
     C = _run_dense(tg, dt, A, B, "row", out, pad=8)
-    rows = None if M * N * K <= 2**29 else np.r_[0:8, M // 2 : M // 2 + 8, M - 8 : M]
-    _check(C, A, B, dt, "row", out, rows=rows)
+    _check(C, A, B, dt, "row", out)
 
 
 def test_row_major_b_large(tg):
     M = N = K = 2048
     A, B, _, _ = _inputs("bf16", M, N, K, "row", seed=77)
     C = _run_dense(tg, "bf16", A, B, "row", "bf16")
-    _check(C, A, B, "bf16", "row", "bf16", rows=np.r_[0:8, 1020:1028, 2040:2048])
+    _check(C, A, B, "bf16", "row", "bf16")
     C2 = _run_dense(tg, "bf16", A, B, "row", "bf16")
     assert torch.equal(C, C2), "repeated runs differ"
 
@@ -262,8 +287,7 @@ def test_medium_multi_tile(tg, dt, lay):
     for M, N, K in [(1280, 1288, 200), (3600, 3400, 136)]:
         A, B, sa, sb = _inputs(dt, M, N, K, lay, seed=M + K)
         C = _run_dense(tg, dt, A, B, lay, "f32", scale_a=sa, scale_b=sb)
-        rows = np.r_[0:40, M // 2 - 20 : M // 2 + 20, M - 40 : M]
-        _check(C, A, B, dt, lay, "f32", sa, sb, rows=rows)
+        _check(C, A, B, dt, lay, "f32", sa, sb, inner_rel=_fp8_inner(dt, M, N, K, "f32"))
 
 
 def _random_cases(n=30, seed=2024):
@@ -291,7 +315,7 @@ def test_random_shapes(tg, case):
     dt, lay, out, M, N, K = case
     A, B, sa, sb = _inputs(dt, M, N, K, lay, seed=M * 7 + N * 3 + K)
     C = _run_dense(tg, dt, A, B, lay, out, scale_a=sa, scale_b=sb)
-    _check(C, A, B, dt, lay, out, sa, sb)
+    _check(C, A, B, dt, lay, out, sa, sb, inner_rel=_fp8_inner(dt, M, N, K, out))
 
 
 # The 128 tile takes an 8-deep LDS ring up to 256 tiles and a 4-deep one
@@ -304,8 +328,7 @@ def test_ring_depth_boundary(tg, dt, lay, shape):
     M, N, K = shape
     A, B, sa, sb = _inputs(dt, M, N, K, lay, seed=M + N + K)
     C = _run_dense(tg, dt, A, B, lay, "f32", scale_a=sa, scale_b=sb)
-    rows = np.r_[0:16, M // 2 : M // 2 + 16, M - 16 : M]
-    _check(C, A, B, dt, lay, "f32", sa, sb, rows=rows)
+    _check(C, A, B, dt, lay, "f32", sa, sb)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp8"])
@@ -316,8 +339,7 @@ def test_large_ragged_16bit_out(tg, dt, out):
     M, N, K = 3600, 3404, 272  # K a multiple of 16: the NT kernel for fp8 too
     A, B, sa, sb = _inputs(dt, M, N, K, "col", seed=N + K)
     C = _run_dense(tg, dt, A, B, "col", out, scale_a=sa, scale_b=sb)
-    rows = np.r_[0:24, 1800:1824, M - 24 : M]
-    _check(C, A, B, dt, "col", out, sa, sb, rows=rows)
+    _check(C, A, B, dt, "col", out, sa, sb)
 
 
 # Leading dimensions so large that the buffer offsets of the fast kernels
@@ -538,6 +560,52 @@ def test_w4a16_decode_lds_strided(tg):
     assert torch.isnan(Cbuf[:, N:]).all()
 
 
+# One-hot rows of A select single weights: C[i][n] = W[n][k_i] with one
+# nonzero product per output, so each w4a16 GEMM kernel's in-register
+# dequant must give exactly tg_dequant_w4's (and the oracle's) fp16 weight.
+# One case per kernel, as the host dispatches them: the 64 x 128 tile kernel
+# (K a multiple of 256), the LDS decode kernel (K a multiple of 1024) at one
+# row, at 16 rows and in 16-row slices, the register decode kernel (K not a
+# multiple of 1024), and the generic tile kernel on both its tile sizes (K
+# not a multiple of 256).
+W4_ONE_HOT = {
+    "gemm_w4": (256, 1032, 2048),
+    "skinny_w4_lds_m1": (1, 520, 2048),
+    "skinny_w4_lds_m16": (16, 520, 3072),
+    "skinny_w4_lds_slices": (40, 264, 1024),
+    "skinny_w4": (16, 200, 1152),
+    "tile_gemm_w4_64": (100, 520, 640),
+    "tile_gemm_w4_128": (1300, 1300, 384),
+}
+
+
+@pytest.mark.parametrize("zp", [3, 8])
+@pytest.mark.parametrize("kernel", list(W4_ONE_HOT))
+def test_w4a16_one_hot_matches_dequant(tg, kernel, zp):
+    M, N, K = W4_ONE_HOT[kernel]
+    _, q, s = _w4_inputs(1, N, K, seed=len(kernel) + 11 * zp)
+    qd, sd = q.cuda(), s.cuda()
+    W = torch.empty((N, K), dtype=torch.float16, device="cuda")
+    tg.tg_dequant_w4(qd, sd, W, K, zero_point=zp)
+    gen = torch.Generator().manual_seed(M + K)
+    # several rounds at one row; else one k per row, every word slot and
+    # scale group covered (k_i = i scattered, the rest random)
+    rounds = 8 if M == 1 else 1
+    Wh = W.cpu()
+    for _ in range(rounds):
+        ks = torch.randint(0, K, (M,), generator=gen)
+        if M > 1:
+            ks[: min(M, 16)] = torch.arange(min(M, 16)) * (K // 16) + torch.arange(min(M, 16)) % 8
+        A = torch.zeros((M, K), dtype=torch.float16)
+        A[torch.arange(M), ks] = 1.0
+        C = torch.full((M, (N + 7) // 8 * 8), float("nan"), dtype=torch.float16, device="cuda")[:, :N]
+        tg.tg_gemm_w4a16(A.cuda(), qd, sd, C, group_size=128, zero_point=zp)
+        torch.cuda.synchronize()
+        ref = Wh.t()[ks]  # row i: W[:, k_i]
+        assert torch.equal(C.cpu().view(torch.int16), ref.view(torch.int16)), kernel
+    assert np.array_equal(Wh.view(torch.int16).numpy().view(np.uint16), oracle.dequant_w4(q, s, K, 128, zp))
+
+
 @pytest.mark.parametrize("zp", [0, 8, 15])
 def test_dequant_bit_exact(tg, zp):
     N, K = 300, 1024
@@ -572,12 +640,59 @@ def test_workload_f16_256(tg):
 
 
 def test_workload_bf16_4096(tg):
+    """The headline workload, every one of its 16.8 M outputs against the oracle."""
     w = synth.workload("bf16_4096")
     C1 = _run_dense(tg, "bf16", w["A"], w["B"], "col", "bf16")
-    rows = np.r_[0:16, 1000:1016, 2040:2056, 4080:4096]
-    _check(C1, w["A"], w["B"], "bf16", "col", "bf16", rows=rows)
+    _check(C1, w["A"], w["B"], "bf16", "col", "bf16")
     C2 = _run_dense(tg, "bf16", w["A"], w["B"], "col", "bf16")
     assert torch.equal(C1, C2), "repeated runs differ"
+
+
+def _exact_256_inputs(dt, n, seed):
+    """A column-major B of n x n random values of the input type, exactly
+    representable in the bf16 output (e4m3 and bf16 values are)."""
+    if dt == "fp8":
+        B, _ = synth.quantize_e4m3(synth.normal((n, n), seed))
+        return B
+    return synth.normal((n, n), seed).to(TDT[dt])
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_exact_identity_permutation_256_tile(tg, dt, out):
+    """The 256 x 256 tile kernels (bf16: 2 LDS stages; fp8: the five-slot
+    ring) at the headline size 4096^3 on inputs with exactly representable
+    results: C = I.B and C = P.B (P a permutation) equal B's entries bit for
+    bit, through the bf16 staged epilogue and the fp32 one.  Each output sums
+    one nonzero product, so any misplaced, dropped or doubled k term, stage
+    or tile shows as a wrong bit."""
+    n = 4096
+    Bs = _exact_256_inputs(dt, n, 900)          # stored N x K: C[i][j] = sum_k A[i][k] Bs[j][k]
+    Bt = Bs.float().t().contiguous()            # Bt[k][j] = Bs[j][k]
+    eye = torch.eye(n).to(TDT[dt])
+    C = _run_dense(tg, dt, eye, Bs, "col", out)
+    assert torch.equal(C.float().cpu(), Bt), "I.B differs from B"
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(901))
+    P = torch.zeros((n, n))
+    P[torch.arange(n), perm] = 1.0               # row i of P.B is row perm[i] of B
+    C = _run_dense(tg, dt, P.to(TDT[dt]), Bs, "col", out)
+    assert torch.equal(C.float().cpu(), Bt[perm]), "P.B differs from the permuted B"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_exact_one_hot_256_tile(tg, dt):
+    """One-hot rows of A at scattered k (one per row, every k position class
+    of the K step and the MFMA sub-steps), scales 1, fp32 output, on the
+    256 x 256 tile: C[i][j] = B[k_i][j] exactly."""
+    M, N, K = 3584, 3584, 2048  # 196 tiles of 256: the 256 tile
+    Bs = _exact_256_inputs(dt, N, 902)[:, :K].contiguous() if N >= K else None
+    ks = torch.randint(0, K, (M,), generator=torch.Generator().manual_seed(903))
+    ks[:K] = torch.arange(K)  # every k once
+    A = torch.zeros((M, K))
+    A[torch.arange(M), ks] = 1.0
+    C = _run_dense(tg, dt, A.to(TDT[dt]), Bs, "col", "f32")
+    ref = Bs.float().t()[ks]
+    assert torch.equal(C.cpu(), ref)
 
 
 def test_workload_bf16_skinny(tg):
@@ -587,11 +702,10 @@ def test_workload_bf16_skinny(tg):
 
 
 def test_workload_fp8_8192(tg):
+    """The fp8 workload, every one of its 67 M outputs against the oracle."""
     w = synth.workload("fp8_8192")
     C = _run_dense(tg, "fp8", w["A"], w["B"], "col", "bf16", scale_a=w["scale_a"], scale_b=w["scale_b"])
-    rows = np.r_[0:8, 4100:4104, 8188:8192]
-    # the workload's bf16 output meets the plain bound, without the fp8 inner-sum term
-    _check(C, w["A"], w["B"], "fp8", "col", "bf16", w["scale_a"], w["scale_b"], rows=rows, inner_rel=0.0)
+    _check(C, w["A"], w["B"], "fp8", "col", "bf16", w["scale_a"], w["scale_b"])
 
 
 def test_fp8_inner_sum_model(tg):
@@ -623,9 +737,8 @@ def test_workload_w4a16(tg):
     w = synth.workload("w4a16")
     A, q, s, K = w["A"], w["qweight"], w["scales"], w["K"]
     C = _run_w4(tg, A, q, s)
-    rows = np.r_[0:8, 128:136, 248:256]
-    cref, S = oracle.w4a16(A[rows], q, s, K)
-    ok, r, idx = ochk.check(_f64(C[rows]), cref, S, K, "f16")
+    cref, S = oracle.w4a16(A, q, s, K)
+    ok, r, idx = ochk.check(_f64(C), cref, S, K, "f16")
     assert ok, (r, idx)
     W = torch.empty((w["N"], K), dtype=torch.float16, device="cuda")
     tg.tg_dequant_w4(q.cuda(), s.cuda(), W, K)
@@ -731,9 +844,8 @@ def test_workload_sp24_4096(tg):
     w = synth.workload("sp24_4096")
     A, v, m, K = w["A"], w["vals"], w["meta"], w["K"]
     C = _run_sp(tg, A, v, m, "bf16")
-    rows = np.r_[0:8, 2040:2048, 4088:4096]
-    cref, S = oracle.gemm_sp24(A[rows], v, m, K)
-    ok, r, idx = ochk.check(_f64(C[rows]), cref, S, K, "bf16")
+    cref, S = oracle.gemm_sp24(A, v, m, K)
+    ok, r, idx = ochk.check(_f64(C), cref, S, K, "bf16")
     assert ok, (r, idx)
 
 
@@ -757,23 +869,20 @@ def test_repeat_bitwise(tg, case):
         A, B, sa, sb = _inputs(dt, M, N, K, "col", seed=REPEAT_CASES.index(case) + 500)
         out = "f32" if case == "skinny" else "bf16"
         outs = [_run_dense(tg, dt, A, B, "col", out, scale_a=sa, scale_b=sb).clone() for _ in range(runs)]
-        rows = np.r_[0:4, M - 4 : M]
-        _check(outs[0], A, B, dt, "col", out, sa, sb, rows=rows)
+        _check(outs[0], A, B, dt, "col", out, sa, sb)
     elif case in ("w4_decode", "w4_gemm"):
         M, N, K = (16, 2048, 8192) if case == "w4_decode" else (256, 1024, 2048)
         A, q, s = _w4_inputs(M, N, K, seed=17)
         outs = [_run_w4(tg, A, q, s).clone() for _ in range(runs)]
-        rows = [0, M - 1]
-        cref, S = oracle.w4a16(A[rows], q, s, K)
-        ok, r, idx = ochk.check(_f64(outs[0][rows]), cref, S, K, "f16")
+        cref, S = oracle.w4a16(A, q, s, K)
+        ok, r, idx = ochk.check(_f64(outs[0]), cref, S, K, "f16")
         assert ok, (r, idx)
     else:
         M, N, K = 512, 1024, 2048
         A, v, m = _sp_inputs(M, N, K, seed=23)
         outs = [_run_sp(tg, A, v, m, "bf16").clone() for _ in range(runs)]
-        rows = [0, M - 1]
-        cref, S = oracle.gemm_sp24(A[rows], v, m, K)
-        ok, r, idx = ochk.check(_f64(outs[0][rows]), cref, S, K, "bf16")
+        cref, S = oracle.gemm_sp24(A, v, m, K)
+        ok, r, idx = ochk.check(_f64(outs[0]), cref, S, K, "bf16")
         assert ok, (r, idx)
     for i, o in enumerate(outs[1:], 1):
         assert torch.equal(o, outs[0]), f"launch {i} differs from launch 0"
