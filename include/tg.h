@@ -19,9 +19,9 @@
  * 生态互操作、性能、局限与路线图.
  *
  * Conventions shared by every entry point
- *  - Pointers A, B, C, qweight, scales, W, Wv, Wm are DEVICE pointers owned by the
- *    caller.  The library never allocates, frees or retains them and keeps no
- *    state between calls (it is reentrant).
+ *  - Pointers A, B, C, qweight, scales, W, Wv, Wm, workspace are DEVICE
+ *    pointers owned by the caller.  The library never allocates, frees or
+ *    retains them and keeps no state between calls (it is reentrant).
  *  - Matrices are row-major with a leading dimension in ELEMENTS:
  *      A      : M x K, element (i,k) at A[i*lda + k], lda >= K
  *      B      : TG_ROW_MAJOR: K x N, element (k,j) at B[k*ldb + j], ldb >= N
@@ -152,6 +152,51 @@ tg_status tg_gemm_sp24_bf16(int64_t M, int64_t N, int64_t K,
                             const void *Wm, int64_t ldm,
                             void *C, int64_t ldc, tg_dtype c_dtype,
                             void *stream);
+
+/* Input element type of tg_gemm_ex. */
+typedef enum { TG_IN_F16 = 0, TG_IN_BF16 = 1, TG_IN_FP8 = 2 } tg_input;
+
+/* Bytes of workspace tg_gemm_ex can use for this problem to split its K
+ * range over several workgroups per output tile (0: it never splits this
+ * problem, a NULL workspace is then as good as any); -1 for a negative size
+ * or an invalid enum.  Depends only on the arguments given (not on leading
+ * dimensions or output type), so it may be queried once per shape. */
+int64_t tg_gemm_ex_workspace_bytes(tg_input in, int64_t M, int64_t N, int64_t K,
+                                   tg_layout b_layout);
+
+/* The dense GEMM of tg_gemm_f16 / tg_gemm_bf16 / tg_gemm_fp8 (selected by
+ * `in`; same operands, layouts, conventions and results) with a workspace
+ * that lets the library split K over several workgroups per output tile
+ * where too few output tiles would leave the chip's compute units idle or
+ * re-read the operands too often (e.g. a few hundred rows against an
+ * 8192 x 8192 weight).  This is the split of K whose partial results are
+ * summed on chip in the TileScale README's GEMM example (section "Example
+ * of GEMM"), taken across workgroups: each workgroup accumulates its K
+ * range in fp32, stores the fp32 partial tile in the workspace, and the
+ * last one to finish adds the partial tiles in split order (a fixed order:
+ * repeated calls give bit-identical results) and stores C.
+ *   scale_a, scale_b : used for TG_IN_FP8 only (finite), ignored otherwise.
+ *   workspace        : caller-owned DEVICE memory of workspace_bytes bytes,
+ *                      256-byte aligned, or NULL (workspace_bytes 0: no
+ *                      split, exactly the plain entry point).  Its first
+ *                      64 KiB hold arrival counters: they must be zero
+ *                      before the workspace's first use (zero-fill it once)
+ *                      and every call leaves them zero when it completes,
+ *                      so one workspace serves any later call of any shape.
+ *                      The rest holds partial tiles (scratch, never cleared).
+ *                      Calls that run at the same time (e.g. on two streams)
+ *                      must use different workspaces.
+ * Errors: TG_ERR_INVALID_VALUE for an invalid `in`, a negative
+ * workspace_bytes, a NULL workspace with workspace_bytes != 0, or a
+ * workspace smaller than tg_gemm_ex_workspace_bytes reports; TG_ERR_MISALIGNED
+ * for a workspace not 256-byte aligned; otherwise as the plain entry point. */
+tg_status tg_gemm_ex(tg_input in, int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda,
+                     const void *B, int64_t ldb, tg_layout b_layout,
+                     float scale_a, float scale_b,
+                     void *C, int64_t ldc, tg_dtype c_dtype,
+                     void *workspace, int64_t workspace_bytes,
+                     void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *tg_status_string(tg_status status);

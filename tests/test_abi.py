@@ -23,7 +23,8 @@ def tg():
 
 def test_header_declares_expected_entry_points():
     assert _declared() == sorted(["tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16",
-                                  "tg_dequant_w4", "tg_gemm_sp24_bf16", "tg_status_string", "tg_version"])
+                                  "tg_dequant_w4", "tg_gemm_sp24_bf16", "tg_gemm_ex", "tg_gemm_ex_workspace_bytes",
+                                  "tg_status_string", "tg_version"])
 
 
 def test_library_exports_every_declared_symbol(tg):
@@ -181,3 +182,26 @@ def test_package_imports_without_the_library(tmp_path):
                        timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "raised True", r.stdout
+
+
+def test_gemm_ex_validation(tg):
+    """tg_gemm_ex rejects bad workspace arguments before any HIP call."""
+    lib = tg.lib
+    W = 1 << 20  # a fake 256-byte aligned device address: validation never dereferences it
+
+    def call(inp=1, M=256, N=8192, K=8192, lda=8192, ldb=8192, ws=W, nbytes=1 << 30, lay=1):
+        return lib.tg_gemm_ex(inp, M, N, K, W, lda, W, ldb, lay, 1.0, 1.0, W, N, 2, ws, nbytes, None)
+
+    need = lib.tg_gemm_ex_workspace_bytes(1, 256, 8192, 8192, 1)
+    assert need > 65536
+    assert lib.tg_gemm_ex_workspace_bytes(1, -1, 8, 8, 1) == -1
+    assert lib.tg_gemm_ex_workspace_bytes(7, 8, 8, 8, 1) == -1
+    assert lib.tg_gemm_ex_workspace_bytes(1, 4096, 4096, 4096, 1) == 0  # enough tiles: no split
+    assert call(inp=5) == tg.TG_ERR_INVALID_VALUE
+    assert call(nbytes=-1) == tg.TG_ERR_INVALID_VALUE
+    assert call(ws=None, nbytes=256) == tg.TG_ERR_INVALID_VALUE
+    assert call(nbytes=need - 1) == tg.TG_ERR_INVALID_VALUE  # smaller than the query reports
+    assert call(ws=W + 16) == tg.TG_ERR_MISALIGNED          # not 256-byte aligned
+    assert call(M=-1) == tg.TG_ERR_INVALID_VALUE
+    assert call(M=0) == tg.TG_OK and call(N=0) == tg.TG_OK
+    assert call(lda=8) == tg.TG_ERR_INVALID_VALUE            # the dense checks still apply

@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
     tg_gemm_fp8(A, B, C, scale_a, scale_b, b_layout="col", stream=None)
     tg_gemm_w4a16(A, qweight, scales, C, group_size=128, zero_point=8, stream=None)
     tg_dequant_w4(qweight, scales, W, K, group_size=128, zero_point=8, stream=None)
+    tg_gemm_ex(A, B, C, b_layout="col", scale_a=1.0, scale_b=1.0, workspace=None, stream=None)
+    tg_gemm_ex_workspace_bytes(dtype, M, N, K, b_layout="col")
     tg_status_string(code), tg_version()
 
 Tensor conventions: A is M x K; for b_layout "row" B is the K x N matrix, for
@@ -37,8 +39,10 @@ TG_OK, TG_ERR_INVALID_VALUE, TG_ERR_NOT_SUPPORTED, TG_ERR_MISALIGNED, TG_ERR_LAU
 TG_F32, TG_F16, TG_BF16 = 0, 1, 2
 TG_ROW_MAJOR, TG_COL_MAJOR = 0, 1
 
+TG_IN_F16, TG_IN_BF16, TG_IN_FP8 = range(3)
+
 EXPORTS = ("tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16", "tg_dequant_w4",
-           "tg_gemm_sp24_bf16", "tg_status_string", "tg_version")
+           "tg_gemm_sp24_bf16", "tg_gemm_ex", "tg_gemm_ex_workspace_bytes", "tg_status_string", "tg_version")
 
 
 class TGError(RuntimeError):
@@ -64,6 +68,10 @@ def _load() -> ctypes.CDLL:
     for name in ("tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16", "tg_dequant_w4",
                  "tg_gemm_sp24_bf16"):
         getattr(lib, name).restype = ci
+    lib.tg_gemm_ex.argtypes = [ci, i64, i64, i64, vp, i64, vp, i64, ci, f32, f32, vp, i64, ci, vp, i64, vp]
+    lib.tg_gemm_ex.restype = ci
+    lib.tg_gemm_ex_workspace_bytes.argtypes = [ci, i64, i64, i64, ci]
+    lib.tg_gemm_ex_workspace_bytes.restype = i64
     lib.tg_status_string.argtypes = [ci]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_version.argtypes = []
@@ -183,6 +191,38 @@ def tg_gemm_fp8(A, B, C, scale_a: float, scale_b: float, b_layout: str = "col", 
     M, N, K, pa, lda, pb, ldb, lay, pc, ldc, cd, st = _dense("tg_gemm_fp8", A, B, C, b_layout, stream)
     _ok("tg_gemm_fp8", load().tg_gemm_fp8(M, N, K, pa, lda, pb, ldb, lay, float(scale_a), float(scale_b),
                                        pc, ldc, cd, st))
+
+
+_IN = {torch.float16: TG_IN_F16, torch.bfloat16: TG_IN_BF16, torch.float8_e4m3fn: TG_IN_FP8}
+
+
+def tg_gemm_ex_workspace_bytes(dtype, M: int, N: int, K: int, b_layout: str = "col") -> int:
+    """Workspace bytes tg_gemm_ex can use for this problem (0: it never splits K)."""
+    if dtype not in _IN:
+        raise ValueError(f"unsupported input dtype {dtype}")
+    lay = {"row": TG_ROW_MAJOR, "col": TG_COL_MAJOR}[b_layout]
+    n = int(load().tg_gemm_ex_workspace_bytes(_IN[dtype], int(M), int(N), int(K), lay))
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return n
+
+
+def tg_gemm_ex(A, B, C, b_layout: str = "col", scale_a: float = 1.0, scale_b: float = 1.0, workspace=None,
+               stream=None) -> None:
+    """C = A.B (scaled for fp8) with an optional workspace tensor (device memory,
+    256-byte aligned, zero before its first use) that lets K split over
+    workgroups; see include/tg.h."""
+    if A.dtype not in _IN or B.dtype != A.dtype:
+        raise ValueError("tg_gemm_ex takes A and B of one of float16, bfloat16, float8_e4m3fn")
+    M, N, K, pa, lda, pb, ldb, lay, pc, ldc, cd, st = _dense("tg_gemm_ex", A, B, C, b_layout, stream)
+    if workspace is None:
+        pw, nw = None, 0
+    else:
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        pw, nw = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _ok("tg_gemm_ex", load().tg_gemm_ex(_IN[A.dtype], M, N, K, pa, lda, pb, ldb, lay, float(scale_a),
+                                        float(scale_b), pc, ldc, cd, pw, nw, st))
 
 
 def tg_gemm_w4a16(A, qweight, scales, C, group_size: int = 128, zero_point: int = 8, stream=None) -> None:

@@ -206,25 +206,109 @@ __device__ __forceinline__ u32x4 dequant_w4_word(uint32_t w, W4Consts c, f16x2 s
 }
 
 // ------------------------------------------------------- tile scheduling
-// Map the linear workgroup id to an output tile.  Workgroups are dealt to the
-// 8 XCDs of the chip round-robin (id % 8); consecutive ids are first regrouped
-// so that each XCD receives a contiguous range of tiles, and that range is
-// walked GROUP_M tile rows at a time so the tiles resident on one XCD share
-// rows of A and columns of B in that XCD's L2.
+// Workgroups are dealt to the 8 XCDs of the chip round-robin (id % 8).
+// Consecutive ids are regrouped so that each XCD receives a contiguous range
+// of the work (when the grid is a multiple of 8).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks)
+{
+    return (nblocks & 7u) == 0u ? (bid & 7u) * (nblocks >> 3) + (bid >> 3) : bid;
+}
+
+// Tile r (0 .. tiles_m*tiles_n - 1) of a walk that takes group_m tile rows
+// at a time, so that tiles resident together share rows of A and columns
+// of B in their XCD's L2.
+__device__ __forceinline__ void group_walk(uint32_t r, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
+                                           uint32_t& tm, uint32_t& tn)
+{
+    uint32_t per_group = group_m * tiles_n;
+    uint32_t g = r / per_group;
+    uint32_t first_m = g * group_m;
+    uint32_t gsize = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+    uint32_t q = r - g * per_group;
+    tm = first_m + q % gsize;
+    tn = q / gsize;
+}
+
+// Map the linear workgroup id to an output tile (XCD-aware, grouped walk).
 __device__ __forceinline__ void tile_coords(uint32_t bid, uint32_t nblocks, uint32_t tiles_m,
                                             uint32_t tiles_n, uint32_t group_m, uint32_t& tm,
                                             uint32_t& tn)
 {
-    uint32_t idx = bid;
-    if ((nblocks & 7u) == 0u)
-        idx = (bid & 7u) * (nblocks >> 3) + (bid >> 3);
-    uint32_t per_group = group_m * tiles_n;
-    uint32_t g = idx / per_group;
-    uint32_t first_m = g * group_m;
-    uint32_t gsize = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
-    uint32_t r = idx - g * per_group;
-    tm = first_m + r % gsize;
-    tn = r / gsize;
+    group_walk(xcd_remap(bid, nblocks), tiles_m, tiles_n, group_m, tm, tn);
+}
+
+// With K split over `splits` workgroups per tile (the grid is tiles x
+// splits): the remapped id gives the split (slowest) and the tile, so an
+// XCD's contiguous range holds neighbouring tiles of one K range, which
+// share their A and B K-slices in its L2.
+__device__ __forceinline__ void tile_split_coords(uint32_t bid, uint32_t nblocks, uint32_t tiles_m,
+                                                  uint32_t tiles_n, uint32_t splits, uint32_t group_m,
+                                                  uint32_t& tm, uint32_t& tn, uint32_t& split)
+{
+    const uint32_t idx = xcd_remap(bid, nblocks), tiles = tiles_m * tiles_n;
+    split = idx / tiles;
+    group_walk(idx - split * tiles, tiles_m, tiles_n, group_m, tm, tn);
+    (void)splits;
+}
+
+// ------------------------------------------------------ split-K handoff
+// A K range split over S workgroups per output tile (the TileScale
+// README's split of K whose partial results are summed on chip, section
+// "Example of GEMM", taken across workgroups): each wave that owns a share
+// of the tile stores its fp32 partial share in a workspace slot of its own,
+// then counts itself in at the share's arrival counter.  The wave that
+// arrives last adds the S partials in split order (a fixed order: the
+// result does not depend on which wave arrives last), resets the counter to
+// zero for the next call, and stores the share.  No wave ever waits for
+// another.
+//
+// Layout of a partial share in its slot: value v = 4g + e of accumulator
+// block b of lane l at float ((b*4 + g)*64 + l)*4 + e, so each wave store
+// and load moves 1 KiB of contiguous memory.
+//
+// Coherence across the chip's 8 XCDs (each with its own L2): the partial
+// shares are stored and loaded with the device-scope cache policy (sc1), the
+// bits the compiler gives relaxed agent-scope atomic stores and loads:
+// stores write through to the device-coherent level, loads do not hit a
+// stale L2 line.  So publishing needs only the completion of this wave's
+// stores before it counts in, and the last arrival's loads see every
+// partial once its count says all have arrived -- no whole-L2 write-back or
+// invalidate (buffer_wbl2 / buffer_inv), which made a split launch slower
+// than none.
+constexpr int kCachePolicyDevice = 16;  // sc1
+
+__device__ __forceinline__ void splitk_store(float* slot, int b, int g, uint32_t lane, f32x4 v)
+{
+    const auto r = __builtin_amdgcn_make_buffer_rsrc((void*)slot, (short)0, 0x7FFFFFF0, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(bit_cast<u32x4>(v), r, (int)(((b * 4 + g) * 64 + lane) * 16), 0,
+                                           kCachePolicyDevice);
+}
+
+__device__ __forceinline__ f32x4 splitk_load(const float* slot, int b, int g, uint32_t lane)
+{
+    const auto r = __builtin_amdgcn_make_buffer_rsrc((void*)slot, (short)0, 0x7FFFFFF0, 0x00020000);
+    return bit_cast<f32x4>(
+        __builtin_amdgcn_raw_buffer_load_b128(r, (int)(((b * 4 + g) * 64 + lane) * 16), 0, kCachePolicyDevice));
+}
+
+// Called by every lane of a wave after it stored its partial share; true
+// (in every lane) for the last of the `splits` arrivals at `counter`.  The
+// wave's partial stores have completed (vmcnt 0) before it counts itself in
+// with a device-scope atomic; the last arrival's loads come after its count.
+__device__ __forceinline__ bool splitk_last(uint32_t* counter, uint32_t splits, uint32_t lane)
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint32_t old = 0u;
+    if (lane == 0u)
+        old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readlane(old, 0);
+    asm volatile("" ::: "memory");  // no load of a partial is moved above the count
+    if (old != splits - 1u)
+        return false;
+    // every partial of this share has arrived: the counter is free again
+    if (lane == 0u)
+        __hip_atomic_exchange(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
 }
 
 }  // namespace tg

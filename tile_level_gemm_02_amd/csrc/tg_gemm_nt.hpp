@@ -153,8 +153,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     const int64_t M = p.M, N = p.N, K = p.K;
     const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
     const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
-    uint32_t tmi, tni;
-    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, p.group_m, tmi, tni);
+    // K split over S workgroups per tile (S = 1: none); this workgroup runs
+    // K steps [kt0, kt0 + NK).  The ring below counts steps from kt0; global
+    // offsets use the absolute step kt0 + kt.
+    const uint32_t S = p.splits > 1u ? p.splits : 1u;
+    uint32_t tmi, tni, ks;
+    tile_split_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, S, p.group_m, tmi, tni, ks);
     const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
     const uint32_t ldab = (uint32_t)(p.lda * EB), ldbb = (uint32_t)(p.ldb * EB);
     const int32_t rows_a = (int32_t)(M - m0 < BM ? M - m0 : BM);
@@ -162,6 +166,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     const i32x4_t ra = make_rsrc(p.A + m0 * (int64_t)ldab);
     const i32x4_t rb = make_rsrc(NB ? p.B + n0 * EB : p.B + n0 * (int64_t)ldbb);
     const int64_t KT = (K + KE - 1) / KE;  // K is a multiple of CE on this path
+    const int64_t kt0 = KT * ks / S, NK = KT * (ks + 1) / S - kt0;
 
     // ---- staged layout: row r of a stage operand holds RB bytes of K as CH
     // 16-byte chunks; logical chunk c sits at physical chunk c ^ swz(r), with
@@ -227,11 +232,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         o1 = (h & 1) ? vb1 : va1;
         if constexpr (decltype(edge)::value) {
             if (!(NB && (h & 1))) {  // (N-contiguous B: the K tail is a row check, in copy_half)
-                o0 |= chunk_oob(kt, lchunk0);
-                o1 |= chunk_oob(kt, lchunk1);
+                o0 |= chunk_oob(kt0 + kt, lchunk0);
+                o1 |= chunk_oob(kt0 + kt, lchunk1);
             }
         }
-        const uint32_t past = kt < KT ? 0u : kOutOfRange;
+        const uint32_t past = kt < NK ? 0u : kOutOfRange;
         o0 |= past;
         o1 |= past;
     };
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     // copy instruction q of half-stage h (A of step h/2 for even h, B for odd
     // h), with the offsets o0/o1 of that half-stage
     auto copy_half = [&](auto edge, int64_t h, int q, uint32_t o0, uint32_t o1) __attribute__((always_inline)) {
-        const int64_t kt = h >> 1;
+        const int64_t kt = kt0 + (h >> 1);  // absolute K step
         uint32_t v = (q & 1) ? o1 : o0;
         if (NB && (h & 1)) {  // k rows (w*BI + q)*RPIN + lane/CHN of step kt
             const uint32_t kr = (wave * BI + (uint32_t)q) * RPIN;
@@ -424,17 +429,66 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         wait_copies<(NH - 3) * AI>();  // step 0 landed
         __syncthreads();
         read_frags(0, 0, 0);
-        for (int64_t kt = 0; kt < KT; ++kt)
+        for (int64_t kt = 0; kt < NK; ++kt)
             step(edge, kt);
         wait_copies<0>();  // copies past the last step (zeros) must land before LDS is reused
     };
-    if (KT > 0) {
+    if (NK > 0) {
         if (rows_a == BM && rows_b == BN && K % KE == 0)  // full tiles, no K tail
             run(std::false_type{});
         else
             run(std::true_type{});
     }
     mfma_drain();
+    __syncthreads();  // every wave is done reading the stage buffers (the epilogue reuses them)
+
+    // ---- K split: store this wave's partial share, count in; the last of the
+    // S arrivals adds the S partials in split order and goes on to store the
+    // share, the others are done.  (No barrier follows: each wave stages its
+    // share in its own LDS region.)
+    if (S > 1u) {
+        constexpr int SHARE = TM * TN * 1024;  // floats of a wave's share
+        const uint32_t tile = tmi * tiles_n + tni;
+        float* const share0 = p.partials + ((size_t)tile * S * NW + wave) * SHARE;  // split 0's slot
+        auto slot = [&](uint32_t q) __attribute__((always_inline)) { return share0 + (size_t)q * NW * SHARE; };
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    splitk_store(slot(ks), i * TN + j, g, lane,
+                                 f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]});
+        if (!splitk_last(p.counters + (size_t)tile * NW + wave, S, lane))
+            return;
+        // the S partial shares in split order: acc = p_0, then acc += p_q
+        // for q = 1 .. S-1.  This wave's own share p_ks is already in acc
+        // when ks == 0, else it is read back from its slot like the others.
+        // Loads go out in batches of two accumulator blocks (8 x 16 bytes
+        // per lane) ahead of their adds: one wait per batch, not per load.
+        constexpr int NBLK = TM * TN, BB = NBLK >= 2 ? 2 : 1;
+        for (uint32_t q = ks == 0u ? 1u : 0u; q < S; ++q) {
+            const float* src = slot(q);
+#pragma unroll
+            for (int b0 = 0; b0 < NBLK; b0 += BB) {
+                f32x4 v[BB][4];
+#pragma unroll
+                for (int bb = 0; bb < BB; ++bb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        v[bb][g] = splitk_load(src, b0 + bb, g, lane);
+#pragma unroll
+                for (int bb = 0; bb < BB; ++bb) {
+                    const int i = (b0 + bb) / TN, j = (b0 + bb) % TN;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[i][j][4 * g + e] = q == 0u ? v[bb][g][e] : acc[i][j][4 * g + e] + v[bb][g][e];
+                }
+            }
+        }
+    }
 
     // ---- epilogue
     constexpr int WR = BM / WM, WC = BN / WN;  // this wave's sub-tile
@@ -457,7 +511,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         // rows per pass: the largest of WR, WR/2, WR/4 that fits
         constexpr int PR = PBY / OB >= WR ? WR : (PBY / OB >= WR / 2 ? WR / 2 : WR / 4);
         static_assert(PR % 32 == 0 && WR % PR == 0 && (PR * NCH) % 64 == 0, "fp32 staging passes");
-        __syncthreads();  // every wave is done reading the stage buffers
         uint8_t* ep = lds + wave * PBY;
         float* C = (float*)p.C;
 #pragma unroll
@@ -504,7 +557,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         constexpr int NCH = OB / 16;        // 16-byte chunks per row
         constexpr int WBYTES = WR * OB;     // bytes per wave
         static_assert(NW * WBYTES <= NH * HALF, "epilogue staging must fit the stage buffers");
-        __syncthreads();  // every wave is done reading the stage buffers
         uint8_t* ep = lds + wave * WBYTES;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {

@@ -48,15 +48,19 @@ __device__ __forceinline__ uint32_t sk_swz(uint32_t r, uint32_t c)
 }
 
 // SPLIT: the K stages are also split over gridDim.y workgroups per column
-// block (for narrow N, where N / 16 workgroups leave CUs idle); each adds
-// its partial tile into the fp32 output, which the host has zeroed (fp32
-// atomic adds, so the summation order over the split is not fixed).
-template <int E, int O, int WAVES, int AI, int RING, bool SPLIT = false>
+// block (for narrow N, where N / 16 workgroups leave CUs idle).
+//   SPLIT = 1: each adds its partial tile into the fp32 output, which the
+//              host has zeroed (fp32 atomic adds: the summation order over
+//              the split is not fixed);
+//   SPLIT = 2: each stores its partial tile in a workspace slot and counts
+//              in; the last to arrive adds the partials in split order (a
+//              fixed order) and stores C, of any output type (splitk_last).
+template <int E, int O, int WAVES, int AI, int RING, int SPLIT = 0>
 __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
 {
     typedef typename OutInfo<O>::T OutT;
     static_assert(E == E_F16 || E == E_BF16, "16-bit inputs");
-    static_assert(!SPLIT || O == O_F32, "partial tiles are added in fp32");
+    static_assert(SPLIT != 1 || O == O_F32, "partial tiles are added in fp32");
     constexpr int SLOT = SkinnySlot<AI>::BYTES;
     constexpr int PER = 2 + AI;  // copy instructions per stage
     constexpr int ZERO = WAVES * RING * SLOT;  // 16 zero bytes: A rows past 8*AI
@@ -81,8 +85,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
     const uint8_t* const Ab = p.A + 16 * slice * p.lda * 2;
     const int64_t KS = K / kSkKE;  // whole stages
     // this workgroup's stages [z0, z1), split over its waves in contiguous ranges
-    const int64_t z0 = SPLIT ? KS * blockIdx.y / gridDim.y : 0;
-    const int64_t z1 = SPLIT ? KS * (blockIdx.y + 1) / gridDim.y : KS;
+    const int64_t z0 = SPLIT != 0 ? KS * blockIdx.y / gridDim.y : 0;
+    const int64_t z1 = SPLIT != 0 ? KS * (blockIdx.y + 1) / gridDim.y : KS;
     const int64_t s0 = z0 + (z1 - z0) * wave / WAVES;
     const int64_t nst = z0 + (z1 - z0) * (wave + 1) / WAVES - s0;
     if (tid == 0)
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
 
     // the K tail (K % 64: at most two 32-wide blocks, the last one partial),
     // taken by one wave of the workgroup that holds the end of K
-    if (K % kSkKE != 0 && wave == WAVES - 1 && (!SPLIT || blockIdx.y == gridDim.y - 1)) {
+    if (K % kSkKE != 0 && wave == WAVES - 1 && (SPLIT == 0 || blockIdx.y == gridDim.y - 1)) {
         for (int64_t kb = KS * 2; kb * 32 < K; ++kb) {
             const int64_t k = kb * 32 + h * 8;
             u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
@@ -181,18 +185,34 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
     if (wave == 0) {  // sum over the K split, in wave order
         OutT* C = (OutT*)p.C + 16 * slice * p.ldc;
         const int64_t r = c16;
+        f32x4 sum;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            float sum = red[v * 64 + lane];
+            sum[v] = red[v * 64 + lane];
 #pragma unroll
             for (int w = 1; w < WAVES; ++w)
-                sum += red[(w * 4 + v) * 64 + lane];
+                sum[v] += red[(w * 4 + v) * 64 + lane];
+        }
+        if constexpr (SPLIT == 2) {
+            // this workgroup's partial tile into its slot (1 KiB: one value
+            // quadruple per lane), count in; the last of the gridDim.y
+            // arrivals re-reads all of them and adds them in split order
+            float* const slot0 = p.partials + (size_t)blockIdx.x * gridDim.y * 256;
+            splitk_store(slot0 + blockIdx.y * 256, 0, 0, lane, sum);
+            if (!splitk_last(p.counters + blockIdx.x, gridDim.y, lane))
+                return;
+            sum = splitk_load(slot0, 0, 0, lane);
+            for (uint32_t q = 1; q < gridDim.y; ++q)
+                sum += splitk_load(slot0 + q * 256, 0, 0, lane);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
             const int64_t col = n0 + 4 * h + v;
             if (r < M && col < N) {
-                if constexpr (SPLIT)
-                    atomicAdd((float*)C + r * p.ldc + col, sum);
+                if constexpr (SPLIT == 1)
+                    atomicAdd((float*)C + r * p.ldc + col, sum[v]);
                 else
-                    C[r * p.ldc + col] = convert_out<O>(sum);
+                    C[r * p.ldc + col] = convert_out<O>(sum[v]);
             }
         }
     }

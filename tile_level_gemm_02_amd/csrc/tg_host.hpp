@@ -136,71 +136,162 @@ template <> struct NtRing<E_FP8, 256> { static constexpr int NH = 5; };
 template <int BM, int BN> struct NtWaves { static constexpr int WM = 2, WN = 2; };
 template <> struct NtWaves<256, 256> { static constexpr int WM = 2, WN = 4; };
 
-template <int E, int O, int BM, int BN, int BL = B_KCONTIG, int NH = NtRing<E, BM>::NH>
-tg_status launch_nt(const TileArgs& a, hipStream_t s)
+inline int nt_waves(int tile) { return tile == 256 ? 8 : 4; }
+
+// ---- K split over workgroups (only with a caller workspace)
+//
+// Workspace of a split launch: the first kSplitCounterBytes hold 32-bit
+// arrival counters, one per tile and wave of the launch (zero before the
+// first call, left zero by every call), so one zero fill of a workspace
+// serves every later call whatever its shape; then one fp32 partial share
+// per tile, split and wave (tile x tile floats per tile and split), scratch
+// that needs no clearing.
+constexpr int64_t kSplitCounterBytes = 65536;
+constexpr int64_t kSplitMaxCounters = kSplitCounterBytes / 4;
+
+inline int64_t split_ws_bytes(int64_t tiles, int splits, int64_t tile_elems)
 {
-    const int64_t tiles = n_tiles<BM, BN>(a.M, a.N);
-    if (tiles > 0x7FFFFFFF)
-        return TG_ERR_NOT_SUPPORTED;
-    constexpr int RB = NtStaging<E>::RB;
-    constexpr int WM = NtWaves<BM, BN>::WM, WN = NtWaves<BM, BN>::WN;
-    hipLaunchKernelGGL((gemm_nt<E, O, BM, BN, RB, NH, WM, WN, BL>), dim3((uint32_t)tiles), dim3(64 * WM * WN), 0, s, a);
-    return launched();
+    return splits <= 1 ? 0 : kSplitCounterBytes + tiles * splits * tile_elems * 4;
 }
 
-// The 128 and 64 tiles: a ring of 8 half-stages (4 steps in flight) when the
-// tiles fit the chip at the occupancy that allows (one 128 KiB workgroup, or
-// two of 64 KiB, per CU); else 4, which leaves room for more resident
-// workgroups.  A small tile does little MFMA work per K step, so with 2 steps
-// in flight it waits on copy latency: at N = K = 8192, M = 128 (64 tiles)
-// 96 -> 45 us, M = 256 (128 tiles) 114 -> 77 us; 2048^3 27 -> 21 us.
-// (pick_tile takes the 64 tile only below 96 tiles of 128, i.e. for at
-// most 384 tiles of 64: always the deep ring.)
-template <int E, int O, int BM, int BL>
-tg_status launch_nt_ring(const TileArgs& a, hipStream_t s)
-{
-    if constexpr (BM == 64) {
-        return launch_nt<E, O, 64, 64, BL, 8>(a, s);
-    } else {
-        if (n_tiles<BM, BM>(a.M, a.N) <= 256)
-            return launch_nt<E, O, BM, BM, BL, 8>(a, s);
-        return launch_nt<E, O, BM, BM, BL, 4>(a, s);
-    }
-}
+// Launch plan of the NT kernel: tile edge, LDS ring depth, K split.
+struct NtPlan {
+    int tile, nh, splits;
+    int64_t ws_bytes;  // workspace the plan needs (0 without a split)
+};
 
-template <int E, int O, int BL = B_KCONTIG>
-tg_status launch_nt_sized(TileArgs& a, hipStream_t s)
+// Estimated cycles of one compute unit for an NT launch with tile edge T and
+// S workgroups per tile.  A workgroup's K loop is bound by the larger of its
+// L2 -> LDS copies (about 37 bytes per clock per CU, measured) and its MFMA
+// issue (4096 FLOP per clock per CU, 8192 for fp8); a split adds the store
+// of each partial share and, for the last arrival, the loads of the other
+// S - 1 and its own (device-coherent accesses, about 16 bytes per clock per
+// CU as fitted to splits measured at N = K = 8192); workgroups run in rounds
+// of one per CU.
+inline double nt_cost(int64_t M, int64_t N, int64_t K, int EB, int T, int S)
 {
-    a.group_m = 4;
-    const int t = pick_tile(a.M, a.N, true);
-    if (t == 256)
-        return launch_nt<E, O, 256, 256, BL>(a, s);
-    if constexpr (ElemInfo<E>::bytes == 1 && BL == B_NCONTIG)
-        return launch_nt_ring<E, O, 128, BL>(a, s);  // (nt_eligible_nrow has ruled out the 64 tile)
-    else if (t == 128)
-        return launch_nt_ring<E, O, 128, BL>(a, s);
-    else
-        return launch_nt_ring<E, O, 64, BL>(a, s);
+    const double tiles = (double)(((M + T - 1) / T) * ((N + T - 1) / T));
+    const double kw = (double)K / S;  // K elements per workgroup
+    const double copy = 2.0 * T * kw * EB / 37.0;
+    const double mfma = 2.0 * T * T * kw / (EB == 1 ? 8192.0 : 4096.0);
+    const double red = S > 1 ? (double)T * T * 4.0 * (S + 1) / 16.0 : 0.0;
+    const double fixed = 4000.0;  // ring fill and epilogue
+    const double rounds = (double)((int64_t)(tiles * S + 255.0) / 256);
+    return rounds * ((copy > mfma ? copy : mfma) + red + fixed);
 }
 
 template <int E, int BL>
-tg_status launch_dense(TileArgs& a, int c_dtype, hipStream_t s)
+NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
 {
-    if constexpr (BL == B_KCONTIG) {
-        if (nt_eligible<E>(a)) {
-            switch (c_dtype) {
-            case TG_F32: return launch_nt_sized<E, O_F32>(a, s);
-            case TG_F16: return launch_nt_sized<E, O_F16>(a, s);
-            default: return launch_nt_sized<E, O_BF16>(a, s);
+    constexpr int EB = ElemInfo<E>::bytes;
+    NtPlan p{pick_tile(M, N, true), 4, 1, 0};
+    if (EB == 1 && BL == B_NCONTIG && p.tile < 128)
+        p.tile = 128;  // (nt_eligible_nrow only admits shapes that pick 128 or 256)
+    if (allow_split) {
+        // split candidates on every tile edge, each workgroup keeping at least
+        // 8 K steps, against the unsplit default
+        const int64_t KT = (K + 128 / EB - 1) / (128 / EB);
+        double best = nt_cost(M, N, K, EB, p.tile, 1);
+        // (the 256 tile's 256 KiB partial shares cost more to reduce than its
+        // splits save: measured slower at every M from 320 to 3072, N = K = 8192)
+        for (int T = 64; T <= 128; T *= 2) {
+            if (EB == 1 && BL == B_NCONTIG && T < 128)
+                continue;
+            if (((M + T - 1) / T) * ((N + T - 1) / T) * nt_waves(T) > kSplitMaxCounters)
+                continue;
+            // (only splits that fit the chip in one round: at N = K = 8192,
+            // M = 768, 768 split workgroups measured 8% slower than 384 unsplit)
+            const int64_t tiles_t = ((M + T - 1) / T) * ((N + T - 1) / T);
+            for (int S = 2; S <= 8 && KT / S >= 8 && tiles_t * S <= 256; ++S) {
+                const double c = nt_cost(M, N, K, EB, T, S);
+                if (c < best * 0.97) {  // (a clear gain over the unsplit default)
+                    best = c;
+                    p.tile = T;
+                    p.splits = S;
+                }
             }
         }
-    } else {
-        if (nt_eligible_nrow<E>(a)) {
-            switch (c_dtype) {
-            case TG_F32: return launch_nt_sized<E, O_F32, B_NCONTIG>(a, s);
-            case TG_F16: return launch_nt_sized<E, O_F16, B_NCONTIG>(a, s);
-            default: return launch_nt_sized<E, O_BF16, B_NCONTIG>(a, s);
-            }
+    }
+    const int64_t tiles = ((M + p.tile - 1) / p.tile) * ((N + p.tile - 1) / p.tile);
+    // ring depth: the 256 tile per element type; the 128 and 64 tiles take 8
+    // half-stages (4 steps in flight) when their workgroups fit the chip at
+    // the occupancy that allows (one 128 KiB workgroup, or two of 64 KiB, per
+    // CU), else 4, which leaves room for more resident workgroups.  A small
+    // tile does little MFMA work per K step, so with 2 steps in flight it
+    // waits on copy latency: at N = K = 8192, M = 128 (64 tiles) 96 -> 45 us,
+    // M = 256 (128 tiles) 114 -> 77 us; 2048^3 27 -> 21 us.
+    if (p.tile == 256)
+        p.nh = E == E_FP8 ? NtRing<E_FP8, 256>::NH : NtRing<E, 256>::NH;
+    else if (p.tile == 64)
+        p.nh = 8;
+    else
+        p.nh = tiles * p.splits <= 256 ? 8 : 4;
+    p.ws_bytes = split_ws_bytes(tiles, p.splits, (int64_t)p.tile * p.tile);
+    return p;
+}
+
+template <int E, int O, int BM, int BN, int BL, int NH>
+tg_status launch_nt(const TileArgs& a, int splits, hipStream_t s)
+{
+    const int64_t grid = n_tiles<BM, BN>(a.M, a.N) * splits;
+    if (grid > 0x7FFFFFFF)
+        return TG_ERR_NOT_SUPPORTED;
+    constexpr int RB = NtStaging<E>::RB;
+    constexpr int WM = NtWaves<BM, BN>::WM, WN = NtWaves<BM, BN>::WN;
+    hipLaunchKernelGGL((gemm_nt<E, O, BM, BN, RB, NH, WM, WN, BL>), dim3((uint32_t)grid), dim3(64 * WM * WN), 0, s, a);
+    return launched();
+}
+
+// Launch an NT plan.  With plan.splits > 1, `ws` is a zeroed-counter
+// workspace of at least plan.ws_bytes bytes (256-byte aligned).
+template <int E, int O, int BL>
+tg_status launch_nt_plan(TileArgs& a, const NtPlan& plan, void* ws, hipStream_t s)
+{
+    a.group_m = 4;
+    a.splits = (uint32_t)plan.splits;
+    if (plan.splits > 1) {
+        a.counters = (uint32_t*)ws;
+        a.partials = (float*)((uint8_t*)ws + kSplitCounterBytes);
+    }
+    if (plan.tile == 256) {
+        if (plan.nh == 5)
+            return launch_nt<E, O, 256, 256, BL, 5>(a, plan.splits, s);
+        return launch_nt<E, O, 256, 256, BL, 4>(a, plan.splits, s);
+    }
+    if (plan.tile == 128) {
+        if (plan.nh == 8)
+            return launch_nt<E, O, 128, 128, BL, 8>(a, plan.splits, s);
+        return launch_nt<E, O, 128, 128, BL, 4>(a, plan.splits, s);
+    }
+    if constexpr (ElemInfo<E>::bytes == 1 && BL == B_NCONTIG)
+        return TG_ERR_NOT_SUPPORTED;  // (never planned: 64-byte fp8 B rows)
+    else
+        return launch_nt<E, O, 64, 64, BL, 8>(a, plan.splits, s);
+}
+
+// Whether the NT kernel takes this problem, for either layout of B.
+template <int E, int BL>
+inline bool nt_takes(const TileArgs& a)
+{
+    if constexpr (BL == B_KCONTIG)
+        return nt_eligible<E>(a);
+    else
+        return nt_eligible_nrow<E>(a);
+}
+
+// Dense GEMM launch.  `ws`/`ws_bytes`: a caller workspace (NULL/0 for none);
+// the NT kernel splits K over workgroups only when the plan's workspace fits.
+template <int E, int BL>
+tg_status launch_dense(TileArgs& a, int c_dtype, hipStream_t s, void* ws = nullptr, int64_t ws_bytes = 0)
+{
+    if (nt_takes<E, BL>(a)) {
+        NtPlan plan = plan_nt<E, BL>(a.M, a.N, a.K, ws != nullptr);
+        if (plan.ws_bytes > ws_bytes)
+            plan = plan_nt<E, BL>(a.M, a.N, a.K, false);
+        switch (c_dtype) {
+        case TG_F32: return launch_nt_plan<E, O_F32, BL>(a, plan, ws, s);
+        case TG_F16: return launch_nt_plan<E, O_F16, BL>(a, plan, ws, s);
+        default: return launch_nt_plan<E, O_BF16, BL>(a, plan, ws, s);
         }
     }
     switch (c_dtype) {
@@ -228,7 +319,7 @@ inline int skinny_split(int64_t blocks, int64_t K)
     return split > 1 ? (int)split : 1;
 }
 
-template <int E, int O, int AI, bool SPLIT>
+template <int E, int O, int AI, int SPLIT>
 void launch_skinny_ai(const SkinnyArgs& sa, int64_t blocks, int split, hipStream_t s)
 {
     typedef SkinnyCfg G;
@@ -237,13 +328,32 @@ void launch_skinny_ai(const SkinnyArgs& sa, int64_t blocks, int split, hipStream
 }
 
 // A rows are copied 8 at a time: one copy instruction for M <= 8, two above.
-template <int E, int O, bool SPLIT = false>
+template <int E, int O, int SPLIT = 0>
 void launch_skinny(const SkinnyArgs& sa, int64_t blocks, int split, hipStream_t s)
 {
     if (sa.M <= 8)
         launch_skinny_ai<E, O, 1, SPLIT>(sa, blocks, split, s);
     else
         launch_skinny_ai<E, O, 2, SPLIT>(sa, blocks, split, s);
+}
+
+// Workspace of the skinny kernel's split through partial tiles: the
+// counters (one per workgroup column), then a 1 KiB partial tile per
+// workgroup; 0 where the counters would not fit their region.
+inline int64_t skinny_ws_bytes(int64_t blocks, int split)
+{
+    if (split <= 1 || blocks > kSplitMaxCounters)
+        return 0;
+    return kSplitCounterBytes + blocks * split * 1024;
+}
+
+// Workgroup columns of the skinny kernel: one per 16-column block and 16-row
+// slice of M; with several slices the column blocks are padded to a
+// multiple of 8.
+inline int64_t skinny_blocks(int64_t M, int64_t N)
+{
+    const int64_t nblk = (N + kSkCols - 1) / kSkCols, slices = (M + 15) / 16;
+    return slices == 1 ? nblk : (nblk + 7) / 8 * 8 * slices;
 }
 
 // Batches up to this many rows against a K-contiguous B take the skinny
@@ -257,7 +367,8 @@ constexpr int64_t kSkSliceMaxM = 32;
 // K steps, which stores zeros: the empty sum).
 template <int E>
 tg_status gemm_16bit(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-                     int64_t ldb, int b_layout, void* C, int64_t ldc, int c_dtype, void* stream)
+                     int64_t ldb, int b_layout, void* C, int64_t ldc, int c_dtype, void* stream,
+                     void* ws = nullptr, int64_t ws_bytes = 0)
 {
     bool empty;
     tg_status st = check_dense(M, N, K, A, lda, B, ldb, b_layout, C, ldc, c_dtype, 2, &empty);
@@ -267,17 +378,29 @@ tg_status gemm_16bit(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     typedef SkinnyCfg G;
     if (M <= kSkSliceMaxM && b_layout == TG_COL_MAJOR && K > 0 && skinny_offsets_fit(K, lda, ldb, G::RING)) {
         SkinnyArgs sa{M, N, K, (const uint8_t*)A, lda, (const uint8_t*)B, ldb, C, ldc};
-        // one workgroup per 16-column block and 16-row slice of M; with
-        // several slices the column blocks are padded to a multiple of 8
-        const int64_t nblk = (N + kSkCols - 1) / kSkCols, slices = (M + 15) / 16;
-        const int64_t blocks = slices == 1 ? nblk : (nblk + 7) / 8 * 8 * slices;
+        const int64_t blocks = skinny_blocks(M, N);
         if (blocks > 0x7FFFFFFF)
             return TG_ERR_NOT_SUPPORTED;
         const int split = skinny_split(blocks, K);
-        if (split > 1 && c_dtype == TG_F32) {  // narrow N: split K over workgroups too
-            hipLaunchKernelGGL(zero_f32<>, dim3((uint32_t)((N + 1023) / 1024), (uint32_t)M), dim3(256), 0, s, (float*)C, N, ldc);
-            launch_skinny<E, O_F32, true>(sa, blocks, split, s);
-            return launched();
+        if (split > 1) {  // narrow N: split K over workgroups too
+            const int64_t need = skinny_ws_bytes(blocks, split);
+            if (ws != nullptr && need > 0 && need <= ws_bytes) {
+                // partial tiles in the workspace, the last arrival stores C: any output type
+                sa.counters = (uint32_t*)ws;
+                sa.partials = (float*)((uint8_t*)ws + kSplitCounterBytes);
+                switch (c_dtype) {
+                case TG_F32: launch_skinny<E, O_F32, 2>(sa, blocks, split, s); break;
+                case TG_F16: launch_skinny<E, O_F16, 2>(sa, blocks, split, s); break;
+                default: launch_skinny<E, O_BF16, 2>(sa, blocks, split, s); break;
+                }
+                return launched();
+            }
+            if (c_dtype == TG_F32) {  // no workspace: fp32 atomic adds into a zeroed C
+                hipLaunchKernelGGL(zero_f32<>, dim3((uint32_t)((N + 1023) / 1024), (uint32_t)M), dim3(256), 0, s, (float*)C,
+                                   N, ldc);
+                launch_skinny<E, O_F32, 1>(sa, blocks, split, s);
+                return launched();
+            }
         }
         switch (c_dtype) {
         case TG_F32: launch_skinny<E, O_F32>(sa, blocks, 1, s); break;
@@ -298,8 +421,72 @@ tg_status gemm_16bit(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     a.ldc = ldc;
     a.alpha = 1.0f;
     if (b_layout == TG_COL_MAJOR)
-        return launch_dense<E, B_KCONTIG>(a, c_dtype, s);
-    return launch_dense<E, B_NCONTIG>(a, c_dtype, s);
+        return launch_dense<E, B_KCONTIG>(a, c_dtype, s, ws, ws_bytes);
+    return launch_dense<E, B_NCONTIG>(a, c_dtype, s, ws, ws_bytes);
 }
+
+// fp8 GEMM (validation as for the 16-bit inputs, plus finite scales).
+inline tg_status gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                          int64_t ldb, int b_layout, float scale_a, float scale_b, void* C, int64_t ldc,
+                          int c_dtype, void* stream, void* ws = nullptr, int64_t ws_bytes = 0)
+{
+    bool empty;
+    tg_status st = check_dense(M, N, K, A, lda, B, ldb, b_layout, C, ldc, c_dtype, 1, &empty);
+    if (st != TG_OK || empty)
+        return st;
+    if (!__builtin_isfinite(scale_a) || !__builtin_isfinite(scale_b))
+        return TG_ERR_INVALID_VALUE;
+    TileArgs a{};
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.A = (const uint8_t*)A;
+    a.lda = lda;
+    a.B = (const uint8_t*)B;
+    a.ldb = ldb;
+    a.C = C;
+    a.ldc = ldc;
+    a.alpha = scale_a * scale_b;
+    hipStream_t s = (hipStream_t)stream;
+    if (b_layout == TG_COL_MAJOR)
+        return launch_dense<E_FP8, B_KCONTIG>(a, c_dtype, s, ws, ws_bytes);
+    return launch_dense<E_FP8, B_NCONTIG>(a, c_dtype, s, ws, ws_bytes);
+}
+
+// Workspace a dense call would use for its K split: the skinny kernel's for
+// few rows against a K-contiguous B, else the NT plan's for a problem on the
+// NT kernel's element grid (whole 16-byte chunks along K, and along N for a
+// row-major B); 0 where it never splits.
+template <int E>
+int64_t dense_ws_bytes(int64_t M, int64_t N, int64_t K, int b_layout)
+{
+    constexpr int CE = 16 / ElemInfo<E>::bytes;
+    if (M <= 0 || N <= 0 || K <= 0)
+        return 0;
+    if (E != E_FP8 && M <= kSkSliceMaxM && b_layout == TG_COL_MAJOR) {  // the skinny kernel (any K)
+        const int64_t blocks = skinny_blocks(M, N);
+        return skinny_ws_bytes(blocks, skinny_split(blocks, K));
+    }
+    if (K % CE != 0)
+        return 0;
+    if (b_layout == TG_COL_MAJOR)
+        return plan_nt<E, B_KCONTIG>(M, N, K, true).ws_bytes;
+    if (N % CE != 0)
+        return 0;
+    return plan_nt<E, B_NCONTIG>(M, N, K, true).ws_bytes;
+}
+
+// Per-type entry points with a split workspace, each defined (and its kernels
+// instantiated) in that type's translation unit; tg_gemm_ex dispatches to them.
+tg_status gemm_f16_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                      int b_layout, void* C, int64_t ldc, int c_dtype, void* stream, void* ws, int64_t ws_bytes);
+tg_status gemm_bf16_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       int b_layout, void* C, int64_t ldc, int c_dtype, void* stream, void* ws, int64_t ws_bytes);
+tg_status gemm_fp8_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                      int b_layout, float scale_a, float scale_b, void* C, int64_t ldc, int c_dtype, void* stream,
+                      void* ws, int64_t ws_bytes);
+int64_t ws_bytes_f16(int64_t M, int64_t N, int64_t K, int b_layout);
+int64_t ws_bytes_bf16(int64_t M, int64_t N, int64_t K, int b_layout);
+int64_t ws_bytes_fp8(int64_t M, int64_t N, int64_t K, int b_layout);
 
 }  // namespace tg

@@ -30,6 +30,13 @@ struct TileArgs {
     const uint16_t* scales;
     int64_t lds;  // fp16 elements
     int32_t zero_point;
+    // K split over `splits` workgroups per output tile (1: no split).  With
+    // splits > 1 the kernel takes one arrival counter per tile and wave from
+    // `counters` (all zero on entry, zero again on exit) and one fp32 partial
+    // share per tile, split and wave from `partials` (see splitk_last).
+    uint32_t splits;
+    uint32_t* counters;
+    float* partials;
 };
 
 // B storage: K-contiguous (column-major K x N, i.e. N x K rows) or N-contiguous
@@ -291,6 +298,10 @@ struct SkinnyArgs {
     int64_t ldb;
     void* C;
     int64_t ldc;
+    // K split through a workspace (see skinny_gemm, SPLIT = 2): one arrival
+    // counter per workgroup column, one 1 KiB partial tile per workgroup
+    uint32_t* counters;
+    float* partials;
 };
 
 template <int E> struct Mfma16;
