@@ -56,7 +56,8 @@ typedef enum {
     TG_ERR_INVALID_VALUE = 1, /* negative size, ld too small, NULL pointer, bad enum */
     TG_ERR_NOT_SUPPORTED = 2, /* valid request the library does not implement */
     TG_ERR_MISALIGNED = 3,    /* base pointer or leading dimension not 16-byte aligned */
-    TG_ERR_LAUNCH = 4         /* the HIP runtime refused the launch */
+    TG_ERR_LAUNCH = 4,        /* the HIP runtime refused the launch */
+    TG_ERR_SCRATCH = 5        /* the problem needs more scratch than tg_gemm_ex_noalloc's static buffer */
 } tg_status;
 
 typedef enum { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 } tg_dtype;
@@ -197,6 +198,26 @@ tg_status tg_gemm_ex(tg_input in, int64_t M, int64_t N, int64_t K,
                      void *C, int64_t ldc, tg_dtype c_dtype,
                      void *workspace, int64_t workspace_bytes,
                      void *stream);
+
+/* tg_gemm_ex without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  It allocates nothing: its split
+ * workspace is a static device array of this library, 16 MiB + 64 KiB
+ * (every split plan the library makes fits in it), which each GPU holds from
+ * the library's load until the process ends.  The first call with a device
+ * current looks up that device's array and clears its 64 KiB of arrival
+ * counters with a kernel on `stream`; every call leaves them zero.  Same
+ * arguments (less the workspace), validation, results and errors as
+ * tg_gemm_ex with a workspace of that size, plus TG_ERR_SCRATCH if a problem
+ * would need more scratch than the array holds.  All calls on one GPU share
+ * the array: calls that overlap in time on one GPU (e.g. on two streams)
+ * race and must be serialized by the caller. */
+tg_status tg_gemm_ex_noalloc(tg_input in, int64_t M, int64_t N, int64_t K,
+                             const void *A, int64_t lda,
+                             const void *B, int64_t ldb, tg_layout b_layout,
+                             float scale_a, float scale_b,
+                             void *C, int64_t ldc, tg_dtype c_dtype,
+                             void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *tg_status_string(tg_status status);

@@ -24,7 +24,7 @@ def tg():
 def test_header_declares_expected_entry_points():
     assert _declared() == sorted(["tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16",
                                   "tg_dequant_w4", "tg_gemm_sp24_bf16", "tg_gemm_ex", "tg_gemm_ex_workspace_bytes",
-                                  "tg_status_string", "tg_version"])
+                                  "tg_gemm_ex_noalloc", "tg_status_string", "tg_version"])
 
 
 def test_library_exports_every_declared_symbol(tg):
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(tg):
 
 
 def test_status_strings(tg):
-    for code in range(5):
+    for code in range(6):
         s = tg.tg_status_string(code)
         assert s.startswith("TG_")
     assert "unknown" in tg.tg_status_string(99)
@@ -205,3 +205,22 @@ def test_gemm_ex_validation(tg):
     assert call(M=-1) == tg.TG_ERR_INVALID_VALUE
     assert call(M=0) == tg.TG_OK and call(N=0) == tg.TG_OK
     assert call(lda=8) == tg.TG_ERR_INVALID_VALUE            # the dense checks still apply
+
+
+def test_gemm_ex_noalloc_validation(tg):
+    """tg_gemm_ex_noalloc checks every argument before its first HIP call."""
+    lib = tg.lib
+    W = 1 << 20
+
+    def call(inp=1, M=256, N=8192, K=8192, lda=8192, C=W, cd=2, sa=1.0):
+        return lib.tg_gemm_ex_noalloc(inp, M, N, K, W, lda, W, K, 1, sa, 1.0, C, N, cd, None)
+
+    assert call(inp=9) == tg.TG_ERR_INVALID_VALUE
+    assert call(M=-1) == tg.TG_ERR_INVALID_VALUE
+    assert call(lda=8) == tg.TG_ERR_INVALID_VALUE
+    assert call(C=None) == tg.TG_ERR_INVALID_VALUE
+    assert call(C=W + 2) == tg.TG_ERR_MISALIGNED
+    assert call(cd=7) == tg.TG_ERR_INVALID_VALUE
+    assert call(inp=2, sa=float("nan")) == tg.TG_ERR_INVALID_VALUE
+    assert call(M=0) == tg.TG_OK
+    assert "static buffer" in tg.tg_status_string(tg.TG_ERR_SCRATCH)

@@ -17,6 +17,7 @@ Entry points (same names as the C ABI):
     tg_dequant_w4(qweight, scales, W, K, group_size=128, zero_point=8, stream=None)
     tg_gemm_ex(A, B, C, b_layout="col", scale_a=1.0, scale_b=1.0, workspace=None, stream=None)
     tg_gemm_ex_workspace_bytes(dtype, M, N, K, b_layout="col")
+    tg_gemm_ex_noalloc(A, B, C, b_layout="col", scale_a=1.0, scale_b=1.0, stream=None)
     tg_status_string(code), tg_version()
 
 Tensor conventions: A is M x K; for b_layout "row" B is the K x N matrix, for
@@ -35,14 +36,15 @@ import torch  # loads the HIP runtime that libtg.so then shares
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtg.so")
 
-TG_OK, TG_ERR_INVALID_VALUE, TG_ERR_NOT_SUPPORTED, TG_ERR_MISALIGNED, TG_ERR_LAUNCH = range(5)
+TG_OK, TG_ERR_INVALID_VALUE, TG_ERR_NOT_SUPPORTED, TG_ERR_MISALIGNED, TG_ERR_LAUNCH, TG_ERR_SCRATCH = range(6)
 TG_F32, TG_F16, TG_BF16 = 0, 1, 2
 TG_ROW_MAJOR, TG_COL_MAJOR = 0, 1
 
 TG_IN_F16, TG_IN_BF16, TG_IN_FP8 = range(3)
 
 EXPORTS = ("tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16", "tg_dequant_w4",
-           "tg_gemm_sp24_bf16", "tg_gemm_ex", "tg_gemm_ex_workspace_bytes", "tg_status_string", "tg_version")
+           "tg_gemm_sp24_bf16", "tg_gemm_ex", "tg_gemm_ex_workspace_bytes", "tg_gemm_ex_noalloc",
+           "tg_status_string", "tg_version")
 
 
 class TGError(RuntimeError):
@@ -72,6 +74,8 @@ def _load() -> ctypes.CDLL:
     lib.tg_gemm_ex.restype = ci
     lib.tg_gemm_ex_workspace_bytes.argtypes = [ci, i64, i64, i64, ci]
     lib.tg_gemm_ex_workspace_bytes.restype = i64
+    lib.tg_gemm_ex_noalloc.argtypes = [ci, i64, i64, i64, vp, i64, vp, i64, ci, f32, f32, vp, i64, ci, vp]
+    lib.tg_gemm_ex_noalloc.restype = ci
     lib.tg_status_string.argtypes = [ci]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_version.argtypes = []
@@ -223,6 +227,16 @@ def tg_gemm_ex(A, B, C, b_layout: str = "col", scale_a: float = 1.0, scale_b: fl
         pw, nw = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _ok("tg_gemm_ex", load().tg_gemm_ex(_IN[A.dtype], M, N, K, pa, lda, pb, ldb, lay, float(scale_a),
                                         float(scale_b), pc, ldc, cd, pw, nw, st))
+
+
+def tg_gemm_ex_noalloc(A, B, C, b_layout: str = "col", scale_a: float = 1.0, scale_b: float = 1.0,
+                       stream=None) -> None:
+    """tg_gemm_ex with the library's static scratch in place of a workspace (allocates nothing)."""
+    if A.dtype not in _IN or B.dtype != A.dtype:
+        raise ValueError("tg_gemm_ex_noalloc takes A and B of one of float16, bfloat16, float8_e4m3fn")
+    M, N, K, pa, lda, pb, ldb, lay, pc, ldc, cd, st = _dense("tg_gemm_ex_noalloc", A, B, C, b_layout, stream)
+    _ok("tg_gemm_ex_noalloc", load().tg_gemm_ex_noalloc(_IN[A.dtype], M, N, K, pa, lda, pb, ldb, lay, float(scale_a),
+                                                        float(scale_b), pc, ldc, cd, st))
 
 
 def tg_gemm_w4a16(A, qweight, scales, C, group_size: int = 128, zero_point: int = 8, stream=None) -> None:

@@ -9,6 +9,7 @@ extern "C" const char* tg_status_string(tg_status status)
     case TG_ERR_NOT_SUPPORTED: return "TG_ERR_NOT_SUPPORTED: valid request that this library does not implement";
     case TG_ERR_MISALIGNED: return "TG_ERR_MISALIGNED: base pointer or leading dimension not 16-byte aligned";
     case TG_ERR_LAUNCH: return "TG_ERR_LAUNCH: the HIP runtime refused the kernel launch";
+    case TG_ERR_SCRATCH: return "TG_ERR_SCRATCH: the problem needs more scratch than the library's static buffer holds";
     default: return "unknown tg_status";
     }
 }
