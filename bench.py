@@ -15,7 +15,9 @@ each launch inside the timed region), `cpu_baseline` (the CPU oracle timed
 on a bounded sample of the same workload) and `secondary` (the skinny M=16
 GEMM's GB/s against the HBM peak, the same GEMM on an 8-way column shard
 (N=1024), the fp8 and w4a16 workloads, the w4a16 weights at decode batch
-sizes M=16 and M=1, and the 2:4 sparse GEMM at 4096^3), each
+sizes M=16 and M=1, bf16 M=256 x 8192 x 8192 with and without the split of K
+over workgroups (tg_gemm_ex), the fp8 workload with B row-major, and the
+2:4 sparse GEMM at 4096^3), each
 secondary timed launch by launch with the 256 MB Infinity Cache flushed
 (by a 512 MiB read) before every launch.
 """
@@ -160,6 +162,41 @@ def setup_sp24():
     return w, fn, flops, bytes_
 
 
+def setup_bf16_m256(split: bool):
+    """bf16 M=256, N=K=8192 (a few hundred rows against a large weight), bf16 out:
+    the plain entry point, or tg_gemm_ex with a workspace (K split over workgroups)."""
+    import torch
+    import synth
+    import tile_level_gemm_02_amd as tg
+
+    w = synth.workload("bf16_4096", M=256, N=8192, K=8192)
+    A, B = w["A"].cuda(), w["B"].cuda()
+    C = torch.empty((w["M"], w["N"]), dtype=torch.bfloat16, device="cuda")
+    if split:
+        need = tg.tg_gemm_ex_workspace_bytes(torch.bfloat16, w["M"], w["N"], w["K"])
+        ws = torch.zeros(max(need, 256) // 4, dtype=torch.int32, device="cuda")
+        fn = lambda: tg.tg_gemm_ex(A, B, C, b_layout="col", workspace=ws)
+    else:
+        fn = lambda: tg.tg_gemm_bf16(A, B, C, b_layout="col")
+    M, N, K = w["M"], w["N"], w["K"]
+    return w, fn, 2.0 * M * N * K, 2 * (M * K + N * K + M * N)
+
+
+def setup_fp8_rowb():
+    """The fp8 workload with B stored row-major (K x N): transposing LDS reads."""
+    import torch
+    import synth
+    import tile_level_gemm_02_amd as tg
+
+    w = synth.workload("fp8_8192")
+    A, B = w["A"].cuda(), w["B"].t().contiguous().cuda()
+    C = torch.empty((w["M"], w["N"]), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: tg.tg_gemm_fp8(A, B, C, w["scale_a"], w["scale_b"], b_layout="row")
+    flops = 2.0 * w["M"] * w["N"] * w["K"]
+    bytes_ = w["M"] * w["K"] + w["N"] * w["K"] + 2 * w["M"] * w["N"]
+    return w, fn, flops, bytes_
+
+
 def setup_fp8():
     import torch
     import synth
@@ -197,7 +234,7 @@ def cpu_baseline(target_seconds: float = 12.0):
     import synth
 
     w = synth.workload("bf16_4096")
-    cores = min(16, len(os.sched_getaffinity(0)))
+    cores = len(os.sched_getaffinity(0))  # every core this process may run on
     # time two small row samples, fit t = t0 + rows * per_row, size the sample for ~target_seconds
     def run(r):
         t0 = time.perf_counter()
@@ -212,8 +249,20 @@ def cpu_baseline(target_seconds: float = 12.0):
     dt = run(rows2)
     flops = 2.0 * rows2 * w["N"] * w["K"]
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{rows2} of {w['M']} rows of the bf16 4096^3 product (fp64 triple loop incl. "
-                      f"decode of B), {dt:.1f} s"}
+                      f"decode of B), {dt:.1f} s on {cores} threads"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ------------------------------------------------------------------------ main
@@ -226,10 +275,12 @@ def main():
                     help="untimed launches first: the GPU takes some 20-30 ms of sustained load to reach its clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--back-to-back", action="store_true",
+                    help="with --only: no cache flush between the launches (sustained load, e.g. to sample clocks)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (to scale HBM byte counters)")
-    ap.add_argument("--only", choices=["bf16_4096", "bf16_skinny", "bf16_skinny_n1024", "fp8_8192", "w4a16", "w4a16_m16",
-                                       "w4a16_m1", "sp24_4096"],
+    ap.add_argument("--only", choices=["bf16_4096", "bf16_skinny", "bf16_skinny_n1024", "fp8_8192", "fp8_8192_rowb",
+                                       "w4a16", "w4a16_m16", "w4a16_m1", "sp24_4096", "bf16_m256", "bf16_m256_split"],
                     default=None,
                     help="only run this workload's launches (for counter collection), no JSON line")
     args = ap.parse_args()
@@ -258,14 +309,16 @@ def main():
     flush = make_flush()
     if args.only:
         setup = {"bf16_4096": setup_bf16_4096, "bf16_skinny": setup_skinny, "bf16_skinny_n1024": setup_skinny_shard,
-                 "fp8_8192": setup_fp8,
+                 "fp8_8192": setup_fp8, "fp8_8192_rowb": setup_fp8_rowb,
+                 "bf16_m256": lambda: setup_bf16_m256(False), "bf16_m256_split": lambda: setup_bf16_m256(True),
                  "w4a16": setup_w4a16, "w4a16_m16": lambda: setup_w4a16(16), "sp24_4096": setup_sp24,
                  "w4a16_m1": lambda: setup_w4a16(1)}[args.only]
         _, fn, _, _ = setup()
         for _ in range(args.warmup):
             fn()
         for _ in range(args.steps):
-            flush()
+            if not args.back_to_back:
+                flush()
             fn()
         torch.cuda.synchronize()
         return
@@ -290,6 +343,7 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / avg_launch / 1e12
+
 
     out = {
         "metric": METRIC,
@@ -322,11 +376,14 @@ def main():
                                       ("w4a16", setup_w4a16, "both"),
                                       ("w4a16_m16", lambda: setup_w4a16(16), "hbm"),
                                       ("w4a16_m1", lambda: setup_w4a16(1), "hbm"),
+                                      ("bf16_m256", lambda: setup_bf16_m256(False), "mfma"),
+                                      ("bf16_m256_split", lambda: setup_bf16_m256(True), "mfma"),
+                                      ("fp8_8192_rowb", setup_fp8_rowb, "fp8"),
                                       ("sp24_4096", setup_sp24, "sp")):
             w2, fn2, fl2, by2 = setup()
             for _ in range(3):
                 fn2()
-            ts = time_launches(fn2, n if name != "fp8_8192" else max(10, n // 2), flush=flush)
+            ts = time_launches(fn2, n if not name.startswith("fp8_8192") else max(10, n // 2), flush=flush)
             t = median(ts)
             rec = {"median_us": round(t * 1e6, 3), "min_us": round(min(ts) * 1e6, 3),
                    "TFLOP/s": round(fl2 / t / 1e12, 2), "GB/s": round(by2 / t / 1e9, 1),
