@@ -122,14 +122,18 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2
         const uint32_t lc = (lane % CH) ^ (r % CH);
         va[j] = (int32_t)r < rows_a ? (wq * (BM / 4) + lane / CH) * ldab + lc * 16u : kOutOfRange;
     }
-    // ---- word copies: instruction q of wave quarter w, lane i fetches
-    // 16-byte chunk i % 4 of the 64 bytes of column 32w + 16q + i/4, landing
-    // at byte 64 * (16q + i/4) + 16 * (i % 4) of the quarter's 2 KB
+    // ---- word copies: instruction q of wave quarter w, lane i serves column
+    // c = 16q + i/4 of the quarter and lands at byte 64c + 16(i % 4) of the
+    // quarter's 2 KB, holding the column's 16-byte chunk (i % 4) ^ wsw(c).
+    // The swizzle wsw(c) = (c / 4) % 4 spreads the 16 columns that one pass
+    // of a 16-byte LDS read serves over all 64 banks (unswizzled, the 64-byte
+    // column stride put four columns on each bank group).
+    auto wsw = [](uint32_t c) __attribute__((always_inline)) -> uint32_t { return (c >> 2) & 3u; };
     uint32_t vq[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const uint32_t c = wq * 32u + 16u * q + lane / 4u;
-        vq[q] = (int32_t)c < cols_b ? c * (uint32_t)(p.ldq * 4) + (lane % 4u) * 16u : kOutOfRange;
+        const uint32_t cq = 16u * q + lane / 4u, c = wq * 32u + cq;
+        vq[q] = (int32_t)c < cols_b ? c * (uint32_t)(p.ldq * 4) + ((lane % 4u) ^ wsw(cq)) * 16u : kOutOfRange;
     }
     auto copy_step = [&](uint32_t kt) __attribute__((always_inline)) {
         const uint32_t slot = kt % NA;
@@ -157,11 +161,18 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int i = 0; i < TM; ++i)
             fa[fs][i] = lds128(sa, (i * 32 + lcol) * RB + cs);
     };
+    // this lane's column's scales: row sc_row of lds_s, rotated by sc_rot pairs (see the prologue)
+    const uint32_t half = G / 2;
+    const uint32_t sc_col = wq * 32u + lcol, sc_row = sc_col * half * 4u, sc_rot = sc_col % half;
     auto read_b = [&](uint32_t kt, uint32_t slot) __attribute__((always_inline)) {
         const uint8_t* ws = lds_w + slot * WSTAGE + wq * 2048;
-        words[0] = lds128(ws, lcol * 64u + lhalf * 32u);
-        words[1] = lds128(ws, lcol * 64u + lhalf * 32u + 16u);
-        scale = *(const uint16_t*)(lds_s + ((wq * 32u + lcol) * G + (kt < G ? kt : G - 1u)) * 2u);  // (clamped past the last step)
+        words[0] = lds128(ws, lcol * 64u + (((2u * lhalf) ^ wsw(lcol)) << 4));
+        words[1] = lds128(ws, lcol * 64u + (((2u * lhalf + 1u) ^ wsw(lcol)) << 4));
+        // group kt is in pair kt/2, stored at (kt/2 + rot) mod half (in range
+        // for the stale reads past the last step too: kt/2 <= half)
+        uint32_t pr = kt / 2u + sc_rot;
+        pr = pr >= half ? pr - half : pr;
+        scale = *(const uint16_t*)(lds_s + sc_row + pr * 4u + (kt & 1u) * 2u);
     };
     const W4Consts wc = w4_consts(p.zero_point);
     auto dequant = [&](int s) __attribute__((always_inline)) {
@@ -180,16 +191,20 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2
     };
 
     // ---- prologue: every scale of the tile's columns (column c's G scales
-    // at lds_s + 2*G*c, fetched as G/2 four-byte pairs; instruction t of the
-    // workgroup takes pairs 64t .. 64t+63 of the flattened column-major
-    // array; wave w issues t = w, w+8, ...), then each group's copies of its
-    // first PER-1 steps
+    // in row c of lds_s, 2*G bytes, as G/2 four-byte pairs; instruction t of
+    // the workgroup fills pair positions 64t .. 64t+63 of the flattened rows;
+    // wave w issues t = w, w+8, ...), then each group's copies of its first
+    // PER-1 steps.  Position p of row c holds pair (p - c) mod G/2: a step's
+    // 32 lanes read one group of 32 consecutive columns, which this rotation
+    // puts in 32 distinct banks (unrotated, a row stride of 2*G bytes put
+    // them in two).
     {
-        const uint32_t half = G / 2, pairs = BN * half;
+        const uint32_t pairs = BN * half;
         for (uint32_t t = wave; t * 64u < pairs; t += 8u) {
             const uint32_t e = t * 64u + lane;
-            const uint32_t c = e / half, d = e - c * half;
-            const uint32_t v = (e < pairs && (int32_t)c < cols_b) ? c * (uint32_t)(p.lds * 2) + d * 4u : kOutOfRange;
+            const uint32_t c = e / half, pos = e - c * half;
+            const uint32_t d = pos + half - c % half, dl = d >= half ? d - half : d;
+            const uint32_t v = (e < pairs && (int32_t)c < cols_b) ? c * (uint32_t)(p.lds * 2) + dl * 4u : kOutOfRange;
             load_lds_256(rs, lds_s + t * 256u, v, 0u);
         }
     }
