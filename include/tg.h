@@ -116,6 +116,35 @@ tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K,
                         void *C, int64_t ldc,
                         void *stream);
 
+/* Bytes of workspace tg_gemm_w4a16_ex can use for this problem to split K
+ * over several workgroups per output tile (0: it never splits this problem);
+ * -1 for a negative size. */
+int64_t tg_gemm_w4a16_ex_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* tg_gemm_w4a16 (same operands, formats, limits and results) with a
+ * workspace that lets the library split K over several workgroups per output
+ * tile where the batch has too few rows to fill the chip with its own tiles
+ * (e.g. 256 rows against an 8192 x 8192 weight): a kernel with 128 x 128
+ * tiles, in which each dequantised weight feeds four matrix instructions,
+ * stores fp32 partial tiles in the workspace and the last workgroup of a
+ * tile to finish adds them in split order (repeated calls are bit-identical)
+ * and stores C.  The workspace follows the contract of tg_gemm_ex (device
+ * memory, 256-byte aligned, its first 64 KiB zero before first use and left
+ * zero by every call; one workspace per concurrently running call; NULL with
+ * workspace_bytes 0: exactly tg_gemm_w4a16).  Errors: TG_ERR_INVALID_VALUE
+ * for a negative workspace_bytes, a NULL workspace with workspace_bytes != 0
+ * or a workspace smaller than tg_gemm_w4a16_ex_workspace_bytes reports;
+ * TG_ERR_MISALIGNED for a workspace not 256-byte aligned; otherwise as
+ * tg_gemm_w4a16. */
+tg_status tg_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K,
+                           const void *A, int64_t lda,
+                           const int32_t *qweight, int64_t ldq,
+                           const void *scales, int64_t lds,
+                           int32_t group_size, int32_t zero_point,
+                           void *C, int64_t ldc,
+                           void *workspace, int64_t workspace_bytes,
+                           void *stream);
+
 /* The dequant step of tg_gemm_w4a16 alone: writes W as fp16 [N][K] with
  * leading dimension ldw (W[n*ldw + k]), using the same device routine the
  * GEMM uses, so the two are bit-identical.  Same limits as tg_gemm_w4a16;

@@ -24,7 +24,8 @@ def tg():
 def test_header_declares_expected_entry_points():
     assert _declared() == sorted(["tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16",
                                   "tg_dequant_w4", "tg_gemm_sp24_bf16", "tg_gemm_ex", "tg_gemm_ex_workspace_bytes",
-                                  "tg_gemm_ex_noalloc", "tg_status_string", "tg_version"])
+                                  "tg_gemm_ex_noalloc", "tg_gemm_w4a16_ex", "tg_gemm_w4a16_ex_workspace_bytes",
+                                  "tg_status_string", "tg_version"])
 
 
 def test_library_exports_every_declared_symbol(tg):
@@ -224,3 +225,22 @@ def test_gemm_ex_noalloc_validation(tg):
     assert call(inp=2, sa=float("nan")) == tg.TG_ERR_INVALID_VALUE
     assert call(M=0) == tg.TG_OK
     assert "static buffer" in tg.tg_status_string(tg.TG_ERR_SCRATCH)
+
+
+def test_w4a16_ex_validation(tg):
+    lib = tg.lib
+    W = 1 << 20
+
+    def call(M=256, N=8192, K=8192, ws=W, nbytes=1 << 30, g=128):
+        return lib.tg_gemm_w4a16_ex(M, N, K, W, K, W, K // 8, W, K // 128, g, 8, W, N, ws, nbytes, None)
+
+    need = lib.tg_gemm_w4a16_ex_workspace_bytes(256, 8192, 8192)
+    assert need > 65536
+    assert lib.tg_gemm_w4a16_ex_workspace_bytes(16, 8192, 8192) == 0  # decode sizes: no split
+    assert lib.tg_gemm_w4a16_ex_workspace_bytes(-1, 8, 128) == -1
+    assert call(nbytes=-1) == tg.TG_ERR_INVALID_VALUE
+    assert call(ws=None, nbytes=256) == tg.TG_ERR_INVALID_VALUE
+    assert call(nbytes=need - 1) == tg.TG_ERR_INVALID_VALUE
+    assert call(ws=W + 64) == tg.TG_ERR_MISALIGNED
+    assert call(g=64) == tg.TG_ERR_NOT_SUPPORTED  # the w4a16 checks still apply
+    assert call(M=0) == tg.TG_OK

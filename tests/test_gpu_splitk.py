@@ -185,3 +185,70 @@ def test_skinny_split_workspace(tg, dt, out, shape):
     assert ok, (r, idx)
     C2 = _run(tg, A, B, "col", out, 1.0, 1.0, ws)
     assert torch.equal(C.view(torch.int16) if out != "f32" else C, C2.view(torch.int16) if out != "f32" else C2)
+
+
+# ---------------------------------------------------------------- w4a16
+# tg_gemm_w4a16_ex: the 128 x 128 w4a16 kernel with K split over workgroups
+# (each dequantised word feeds four MFMAs).  The w4a16 workload itself, and
+# ragged rows, columns and K ranges whose split leaves an odd number of
+# scale-group pairs per workgroup.
+
+def _w4_inputs(M, N, K, seed):
+    A = synth.normal((M, K), seed).to(torch.float16)
+    q = synth.random_words((N, K // 8), seed + 1)
+    s = synth.uniform((N, K // 128), seed + 2, 0.005, 0.02).to(torch.float16)
+    return A, q, s
+
+
+def _run_w4_ex(tg, A, q, s, ws, zp=8):
+    M, N = A.shape[0], q.shape[0]
+    C = torch.full((M, (N + 7) // 8 * 8), float("nan"), dtype=torch.float16, device="cuda")[:, :N]
+    tg.tg_gemm_w4a16_ex(A.cuda(), q.cuda(), s.cuda(), C, zero_point=zp, workspace=ws)
+    torch.cuda.synchronize()
+    return C
+
+
+W4_SPLIT = [(256, 8192, 8192), (100, 1000, 4096), (130, 520, 2560), (64, 1024, 8192), (200, 2056, 3072)]
+
+
+@pytest.mark.parametrize("zp", [8, 3])
+@pytest.mark.parametrize("shape", W4_SPLIT, ids=lambda s: "x".join(map(str, s)))
+def test_w4a16_split_parity(tg, shape, zp):
+    M, N, K = shape
+    need = tg.tg_gemm_w4a16_ex_workspace_bytes(M, N, K)
+    assert need > 0, "expected a split plan"
+    A, q, s = _w4_inputs(M, N, K, seed=M + N + K + zp)
+    ws = _shared_workspace(need)
+    C = _run_w4_ex(tg, A, q, s, ws, zp)
+    assert int(ws[:COUNTER_WORDS].count_nonzero()) == 0
+    cref, S = oracle.w4a16(A, q, s, K, zero_point=zp)
+    ok, r, idx = ochk.check(C.float().cpu().double().numpy(), cref, S, K, "f16")
+    assert ok, (r, idx)
+    C2 = _run_w4_ex(tg, A, q, s, ws, zp)
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16)), "repeated split calls differ"
+
+
+def test_w4a16_split_one_hot_matches_dequant(tg):
+    """One-hot rows of A through the split kernel give tg_dequant_w4's weights bit for bit."""
+    M, N, K = 256, 1032, 4096
+    need = tg.tg_gemm_w4a16_ex_workspace_bytes(M, N, K)
+    assert need > 0
+    _, q, s = _w4_inputs(1, N, K, seed=71)
+    W = torch.empty((N, K), dtype=torch.float16, device="cuda")
+    tg.tg_dequant_w4(q.cuda(), s.cuda(), W, K, zero_point=5)
+    ks = torch.randint(0, K, (M,), generator=torch.Generator().manual_seed(72))
+    ks[:16] = torch.arange(16) * (K // 16) + torch.arange(16) % 8
+    A = torch.zeros((M, K), dtype=torch.float16)
+    A[torch.arange(M), ks] = 1.0
+    C = _run_w4_ex(tg, A, q, s, _shared_workspace(need), zp=5)
+    assert torch.equal(C.cpu().view(torch.int16), W.cpu().t()[ks].view(torch.int16))
+
+
+def test_w4a16_ex_without_workspace_is_plain(tg):
+    M, N, K = 256, 1024, 2048
+    A, q, s = _w4_inputs(M, N, K, seed=73)
+    C0 = _run_w4_ex(tg, A, q, s, None)
+    C1 = torch.empty_like(C0)
+    tg.tg_gemm_w4a16(A.cuda(), q.cuda(), s.cuda(), C1)
+    torch.cuda.synchronize()
+    assert torch.equal(C0.view(torch.int16), C1.view(torch.int16))

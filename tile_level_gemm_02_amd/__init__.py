@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
     tg_gemm_ex(A, B, C, b_layout="col", scale_a=1.0, scale_b=1.0, workspace=None, stream=None)
     tg_gemm_ex_workspace_bytes(dtype, M, N, K, b_layout="col")
     tg_gemm_ex_noalloc(A, B, C, b_layout="col", scale_a=1.0, scale_b=1.0, stream=None)
+    tg_gemm_w4a16_ex(A, qweight, scales, C, group_size=128, zero_point=8, workspace=None, stream=None)
+    tg_gemm_w4a16_ex_workspace_bytes(M, N, K)
     tg_status_string(code), tg_version()
 
 Tensor conventions: A is M x K; for b_layout "row" B is the K x N matrix, for
@@ -44,6 +46,7 @@ TG_IN_F16, TG_IN_BF16, TG_IN_FP8 = range(3)
 
 EXPORTS = ("tg_gemm_f16", "tg_gemm_bf16", "tg_gemm_fp8", "tg_gemm_w4a16", "tg_dequant_w4",
            "tg_gemm_sp24_bf16", "tg_gemm_ex", "tg_gemm_ex_workspace_bytes", "tg_gemm_ex_noalloc",
+           "tg_gemm_w4a16_ex", "tg_gemm_w4a16_ex_workspace_bytes",
            "tg_status_string", "tg_version")
 
 
@@ -76,6 +79,10 @@ def _load() -> ctypes.CDLL:
     lib.tg_gemm_ex_workspace_bytes.restype = i64
     lib.tg_gemm_ex_noalloc.argtypes = [ci, i64, i64, i64, vp, i64, vp, i64, ci, f32, f32, vp, i64, ci, vp]
     lib.tg_gemm_ex_noalloc.restype = ci
+    lib.tg_gemm_w4a16_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, i32, vp, i64, vp, i64, vp]
+    lib.tg_gemm_w4a16_ex.restype = ci
+    lib.tg_gemm_w4a16_ex_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.tg_gemm_w4a16_ex_workspace_bytes.restype = i64
     lib.tg_status_string.argtypes = [ci]
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_version.argtypes = []
@@ -253,6 +260,37 @@ def tg_gemm_w4a16(A, qweight, scales, C, group_size: int = 128, zero_point: int 
         raise ValueError("inconsistent w4a16 shapes")
     _ok("tg_gemm_w4a16", load().tg_gemm_w4a16(M, N, K, pa, lda, pq, ldq, ps, lds, int(group_size),
                                            int(zero_point), pc, ldc, _stream(stream)))
+
+
+def tg_gemm_w4a16_ex_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes tg_gemm_w4a16_ex can use for this problem (0: it never splits K)."""
+    n = int(load().tg_gemm_w4a16_ex_workspace_bytes(int(M), int(N), int(K)))
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return n
+
+
+def tg_gemm_w4a16_ex(A, qweight, scales, C, group_size: int = 128, zero_point: int = 8, workspace=None,
+                     stream=None) -> None:
+    """tg_gemm_w4a16 with an optional workspace tensor that lets K split over workgroups."""
+    if A.dtype != torch.float16 or C.dtype != torch.float16:
+        raise ValueError("tg_gemm_w4a16_ex takes float16 A and C")
+    if qweight.dtype != torch.int32 or scales.dtype != torch.float16:
+        raise ValueError("qweight must be int32 and scales float16")
+    M, K, lda, pa = _mat(A, "A")
+    N, _, ldq, pq = _mat(qweight, "qweight")
+    Ns, _, lds, ps = _mat(scales, "scales")
+    Mc, Nc, ldc, pc = _mat(C, "C")
+    if Ns != N or (Mc, Nc) != (M, N):
+        raise ValueError("inconsistent w4a16 shapes")
+    if workspace is None:
+        pw, nw = None, 0
+    else:
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        pw, nw = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _ok("tg_gemm_w4a16_ex", load().tg_gemm_w4a16_ex(M, N, K, pa, lda, pq, ldq, ps, lds, int(group_size),
+                                                    int(zero_point), pc, ldc, pw, nw, _stream(stream)))
 
 
 def tg_dequant_w4(qweight, scales, W, K: int | None = None, group_size: int = 128, zero_point: int = 8,

@@ -2,6 +2,7 @@
 // same device routine, tg::dequant_w4_word, so the GEMM's weights are
 // bit-identical to what tg_dequant_w4 writes.
 #include "tg_gemm_w4.hpp"
+#include "tg_gemm_w4s.hpp"
 #include "tg_host.hpp"
 
 namespace tg {
@@ -119,12 +120,88 @@ bool launch_skinny_lds(const tg::TileArgs& a, hipStream_t s, tg_status* st)
     return true;
 }
 
+// The split kernel gemm_w4s (128 x 128 tiles, K split over S workgroups per
+// tile through a workspace): S = the workgroups that fill the chip in one
+// round (256 / tiles), at most 8, with every split holding whole pairs of
+// scale groups, at least 8 and at most kW4sMaxGroups of them.  Used above
+// the decode batch sizes, for K a multiple of 256 with 4-byte aligned
+// scales of even stride, and 32-bit buffer offsets over a tile; 1 = no split.
+int w4s_splits(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= kW4SliceMaxM || K <= 0 || K % 256 != 0)
+        return 1;
+    const int64_t tiles = tg::n_tiles<128, 128>(M, N), G = K / 128;
+    if (tiles >= 256 || tiles > tg::kSplitMaxCounters)
+        return 1;
+    int64_t S = 256 / tiles;
+    if (S > 8)
+        S = 8;
+    while (S > 1 && G / S < 8)
+        --S;
+    if (S > 1 && (G + S - 1) / S + 2 > tg::kW4sMaxGroups)
+        return 1;
+    return (int)S;
+}
+
+int64_t w4s_ws_bytes(int64_t M, int64_t N, int64_t K)
+{
+    const int S = w4s_splits(M, N, K);
+    return S <= 1 ? 0 : tg::kSplitCounterBytes + tg::n_tiles<128, 128>(M, N) * S * 128 * 128 * 4;
+}
+
+bool w4s_offsets_fit(const tg::TileArgs& a)
+{
+    if (((uintptr_t)a.scales & 3u) != 0 || (a.lds & 1) != 0)
+        return false;
+    const int64_t lim = (int64_t)tg::kNumRecords;
+    return 128 * a.lda * 2 + a.K * 2 + 2048 < lim && 128 * a.ldq * 4 + a.K / 2 + 512 < lim &&
+           128 * a.lds * 2 + a.K / 64 < lim;
+}
+
+tg_status w4a16_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const int32_t* qweight, int64_t ldq,
+                     const void* scales, int64_t lds, int32_t group_size, int32_t zero_point, void* C, int64_t ldc,
+                     void* ws, int64_t ws_bytes, void* stream);
+
 }  // namespace
+
+extern "C" int64_t tg_gemm_w4a16_ex_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return -1;
+    return w4s_ws_bytes(M, N, K);
+}
+
+extern "C" tg_status tg_gemm_w4a16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                      const int32_t* qweight, int64_t ldq, const void* scales, int64_t lds,
+                                      int32_t group_size, int32_t zero_point, void* C, int64_t ldc, void* workspace,
+                                      int64_t workspace_bytes, void* stream)
+{
+    if (workspace_bytes < 0 || (workspace == nullptr && workspace_bytes != 0))
+        return TG_ERR_INVALID_VALUE;
+    if (workspace != nullptr) {
+        if (((uintptr_t)workspace & 255u) != 0)
+            return TG_ERR_MISALIGNED;
+        const int64_t need = tg_gemm_w4a16_ex_workspace_bytes(M, N, K);
+        if (need < 0 || workspace_bytes < need)
+            return TG_ERR_INVALID_VALUE;
+    }
+    return w4a16_impl(M, N, K, A, lda, qweight, ldq, scales, lds, group_size, zero_point, C, ldc, workspace,
+                      workspace_bytes, stream);
+}
 
 extern "C" tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                    const int32_t* qweight, int64_t ldq, const void* scales,
                                    int64_t lds, int32_t group_size, int32_t zero_point, void* C,
                                    int64_t ldc, void* stream)
+{
+    return w4a16_impl(M, N, K, A, lda, qweight, ldq, scales, lds, group_size, zero_point, C, ldc, nullptr, 0, stream);
+}
+
+namespace {
+
+tg_status w4a16_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const int32_t* qweight, int64_t ldq,
+                     const void* scales, int64_t lds, int32_t group_size, int32_t zero_point, void* C, int64_t ldc,
+                     void* ws, int64_t ws_bytes, void* stream)
 {
     if (M < 0)
         return TG_ERR_INVALID_VALUE;
@@ -159,6 +236,17 @@ extern "C" tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* 
     a.lds = lds;
     a.zero_point = zero_point;
     hipStream_t s = (hipStream_t)stream;
+    if (ws != nullptr) {  // the split kernel, where its plan pays and its workspace fits
+        const int S = w4s_splits(M, N, K);
+        if (S > 1 && w4s_ws_bytes(M, N, K) <= ws_bytes && w4s_offsets_fit(a)) {
+            const int64_t tiles = tg::n_tiles<128, 128>(M, N);
+            a.splits = (uint32_t)S;
+            a.counters = (uint32_t*)ws;
+            a.partials = (float*)((uint8_t*)ws + tg::kSplitCounterBytes);
+            hipLaunchKernelGGL((tg::gemm_w4s<6>), dim3((uint32_t)(tiles * S)), dim3(tg::kW4sThreads), 0, s, a);
+            return tg::launched();
+        }
+    }
     if (M <= kW4SliceMaxM) {  // decode: a weight stream, too few output tiles to fill the chip
         tg_status lst = TG_OK;
         if ((M <= 2 && launch_skinny_lds<1>(a, s, &lst)) || (M > 2 && M <= 4 && launch_skinny_lds<2>(a, s, &lst)) ||
@@ -185,6 +273,8 @@ extern "C" tg_status tg_gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* 
         return tg::launch_tile<tg::E_F16, tg::B_KCONTIG, tg::O_F16, 128, 128, true>(a, s);
     return tg::launch_tile<tg::E_F16, tg::B_KCONTIG, tg::O_F16, 64, 64, true>(a, s);
 }
+
+}  // namespace
 
 extern "C" tg_status tg_dequant_w4(int64_t N, int64_t K, const int32_t* qweight, int64_t ldq,
                                    const void* scales, int64_t lds, int32_t group_size,
