@@ -15,8 +15,8 @@ each launch inside the timed region), `cpu_baseline` (the CPU oracle timed
 on a bounded sample of the same workload) and `secondary` (the skinny M=16
 GEMM's GB/s against the HBM peak, the same GEMM on an 8-way column shard
 (N=1024), the fp8 and w4a16 workloads, the w4a16 weights at decode batch
-sizes M=16 and M=1, bf16 M=256 x 8192 x 8192 with and without the split of K
-over workgroups (tg_gemm_ex), the fp8 workload with B row-major, and the
+sizes M=16 and M=1, the w4a16 workload and bf16 M=256 x 8192 x 8192 with
+the split of K over workgroups (tg_gemm_w4a16_ex, tg_gemm_ex) and without, the fp8 workload with B row-major, and the
 2:4 sparse GEMM at 4096^3), each
 secondary timed launch by launch with the 256 MB Infinity Cache flushed
 (by a 512 MiB read) before every launch.
@@ -211,7 +211,8 @@ def setup_fp8():
     return w, fn, flops, bytes_
 
 
-def setup_w4a16(M=None):
+def setup_w4a16(M=None, split=False):
+    """The w4a16 workload (M rows); with split, tg_gemm_w4a16_ex with a workspace (K split over workgroups)."""
     import torch
     import synth
     import tile_level_gemm_02_amd as tg
@@ -219,7 +220,12 @@ def setup_w4a16(M=None):
     w = synth.workload("w4a16", M=M)
     A, q, s = w["A"].cuda(), w["qweight"].cuda(), w["scales"].cuda()
     C = torch.empty((w["M"], w["N"]), dtype=torch.float16, device="cuda")
-    fn = lambda: tg.tg_gemm_w4a16(A, q, s, C)
+    if split:
+        need = tg.tg_gemm_w4a16_ex_workspace_bytes(w["M"], w["N"], w["K"])
+        ws = torch.zeros(max(need, 256) // 4, dtype=torch.int32, device="cuda")
+        fn = lambda: tg.tg_gemm_w4a16_ex(A, q, s, C, workspace=ws)
+    else:
+        fn = lambda: tg.tg_gemm_w4a16(A, q, s, C)
     M, N, K = w["M"], w["N"], w["K"]
     flops = 2.0 * M * N * K
     bytes_ = 2 * M * K + N * K // 2 + 2 * N * (K // 128) + 2 * M * N
@@ -280,7 +286,8 @@ def main():
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (to scale HBM byte counters)")
     ap.add_argument("--only", choices=["bf16_4096", "bf16_skinny", "bf16_skinny_n1024", "fp8_8192", "fp8_8192_rowb",
-                                       "w4a16", "w4a16_m16", "w4a16_m1", "sp24_4096", "bf16_m256", "bf16_m256_split"],
+                                       "w4a16", "w4a16_split", "w4a16_m16", "w4a16_m1", "sp24_4096", "bf16_m256",
+                                       "bf16_m256_split"],
                     default=None,
                     help="only run this workload's launches (for counter collection), no JSON line")
     args = ap.parse_args()
@@ -311,7 +318,7 @@ def main():
         setup = {"bf16_4096": setup_bf16_4096, "bf16_skinny": setup_skinny, "bf16_skinny_n1024": setup_skinny_shard,
                  "fp8_8192": setup_fp8, "fp8_8192_rowb": setup_fp8_rowb,
                  "bf16_m256": lambda: setup_bf16_m256(False), "bf16_m256_split": lambda: setup_bf16_m256(True),
-                 "w4a16": setup_w4a16, "w4a16_m16": lambda: setup_w4a16(16), "sp24_4096": setup_sp24,
+                 "w4a16": setup_w4a16, "w4a16_split": lambda: setup_w4a16(split=True), "w4a16_m16": lambda: setup_w4a16(16), "sp24_4096": setup_sp24,
                  "w4a16_m1": lambda: setup_w4a16(1)}[args.only]
         _, fn, _, _ = setup()
         for _ in range(args.warmup):
@@ -374,6 +381,7 @@ def main():
         for name, setup, peak_key in (("bf16_skinny", setup_skinny, "hbm"), ("bf16_skinny_n1024", setup_skinny_shard, "hbm"),
                                       ("fp8_8192", setup_fp8, "fp8"),
                                       ("w4a16", setup_w4a16, "both"),
+                                      ("w4a16_split", lambda: setup_w4a16(split=True), "both"),
                                       ("w4a16_m16", lambda: setup_w4a16(16), "hbm"),
                                       ("w4a16_m1", lambda: setup_w4a16(1), "hbm"),
                                       ("bf16_m256", lambda: setup_bf16_m256(False), "mfma"),
