@@ -40,7 +40,11 @@
  *    launch returns TG_ERR_LAUNCH.  Faults inside a kernel surface at the
  *    caller's next synchronization.
  *  - Sizes are int64; leading dimensions and sizes must be non-negative and
- *    every index must fit in the addressed buffer (the caller's duty).
+ *    every index must fit in the addressed buffer (the caller's duty).  A
+ *    size or leading dimension above 2^31 - 1 elements returns
+ *    TG_ERR_NOT_SUPPORTED (the workspace queries report 0 for such shapes).
+ *  - Enum arguments are read as the int the C ABI passes: any int is
+ *    accepted, and a value that names no enumerator is TG_ERR_INVALID_VALUE.
  */
 #ifndef TG_H
 #define TG_H

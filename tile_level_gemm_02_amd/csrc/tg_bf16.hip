@@ -5,7 +5,8 @@ extern "C" tg_status tg_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A
                                   const void* B, int64_t ldb, tg_layout b_layout, void* C,
                                   int64_t ldc, tg_dtype c_dtype, void* stream)
 {
-    return tg::gemm_16bit<tg::E_BF16>(M, N, K, A, lda, B, ldb, b_layout, C, ldc, c_dtype, stream);
+    return tg::gemm_16bit<tg::E_BF16>(M, N, K, A, lda, B, ldb, tg::abi_int(b_layout), C, ldc,
+                                      tg::abi_int(c_dtype), stream);
 }
 
 // the same with a split workspace (tg_gemm_ex): instantiated here, once

@@ -1,9 +1,9 @@
 // Library-wide entry points that launch nothing (contract in include/tg.h).
-#include "tg.h"
+#include "tg_abi.hpp"
 
 extern "C" const char* tg_status_string(tg_status status)
 {
-    switch (status) {
+    switch (tg::abi_int(status)) {
     case TG_OK: return "TG_OK: success";
     case TG_ERR_INVALID_VALUE: return "TG_ERR_INVALID_VALUE: invalid size, leading dimension, pointer or enum";
     case TG_ERR_NOT_SUPPORTED: return "TG_ERR_NOT_SUPPORTED: valid request that this library does not implement";

@@ -1,7 +1,7 @@
 // tg_gemm_ex and tg_gemm_ex_workspace_bytes: the dense GEMM of every input
 // type with a caller workspace, which lets the NT kernel split K over
 // several workgroups per output tile (contract in include/tg.h).
-#include "tg.h"
+#include "tg_abi.hpp"
 
 namespace tg {
 tg_status gemm_f16_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -14,34 +14,33 @@ tg_status gemm_fp8_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t ld
 int64_t ws_bytes_f16(int64_t M, int64_t N, int64_t K, int b_layout);
 int64_t ws_bytes_bf16(int64_t M, int64_t N, int64_t K, int b_layout);
 int64_t ws_bytes_fp8(int64_t M, int64_t N, int64_t K, int b_layout);
-}  // namespace tg
 
-namespace {
-
-int64_t ex_ws_bytes(tg_input in, int64_t M, int64_t N, int64_t K, tg_layout b_layout)
-{
-    switch (in) {
-    case TG_IN_F16: return tg::ws_bytes_f16(M, N, K, b_layout);
-    case TG_IN_BF16: return tg::ws_bytes_bf16(M, N, K, b_layout);
-    case TG_IN_FP8: return tg::ws_bytes_fp8(M, N, K, b_layout);
-    default: return -1;
-    }
-}
-
-}  // namespace
-
-extern "C" int64_t tg_gemm_ex_workspace_bytes(tg_input in, int64_t M, int64_t N, int64_t K, tg_layout b_layout)
+// tg_gemm_ex_workspace_bytes on the int values of its enum arguments
+int64_t ex_workspace_bytes(int in, int64_t M, int64_t N, int64_t K, int b_layout)
 {
     if (M < 0 || N < 0 || K < 0 || (b_layout != TG_ROW_MAJOR && b_layout != TG_COL_MAJOR))
         return -1;
-    return ex_ws_bytes(in, M, N, K, b_layout);
+    switch (in) {
+    case TG_IN_F16: return ws_bytes_f16(M, N, K, b_layout);
+    case TG_IN_BF16: return ws_bytes_bf16(M, N, K, b_layout);
+    case TG_IN_FP8: return ws_bytes_fp8(M, N, K, b_layout);
+    default: return -1;
+    }
+}
+}  // namespace tg
+
+extern "C" int64_t tg_gemm_ex_workspace_bytes(tg_input in_arg, int64_t M, int64_t N, int64_t K,
+                                              tg_layout b_layout_arg)
+{
+    return tg::ex_workspace_bytes(tg::abi_int(in_arg), M, N, K, tg::abi_int(b_layout_arg));
 }
 
-extern "C" tg_status tg_gemm_ex(tg_input in, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                                const void* B, int64_t ldb, tg_layout b_layout, float scale_a, float scale_b,
-                                void* C, int64_t ldc, tg_dtype c_dtype, void* workspace, int64_t workspace_bytes,
+extern "C" tg_status tg_gemm_ex(tg_input in_arg, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, tg_layout b_layout_arg, float scale_a, float scale_b,
+                                void* C, int64_t ldc, tg_dtype c_dtype_arg, void* workspace, int64_t workspace_bytes,
                                 void* stream)
 {
+    const int in = tg::abi_int(in_arg), b_layout = tg::abi_int(b_layout_arg), c_dtype = tg::abi_int(c_dtype_arg);
     if (in != TG_IN_F16 && in != TG_IN_BF16 && in != TG_IN_FP8)
         return TG_ERR_INVALID_VALUE;
     if (workspace_bytes < 0 || (workspace == nullptr && workspace_bytes != 0))
@@ -49,7 +48,7 @@ extern "C" tg_status tg_gemm_ex(tg_input in, int64_t M, int64_t N, int64_t K, co
     if (workspace != nullptr) {
         if (((uintptr_t)workspace & 255u) != 0)
             return TG_ERR_MISALIGNED;
-        const int64_t need = tg_gemm_ex_workspace_bytes(in, M, N, K, b_layout);
+        const int64_t need = tg::ex_workspace_bytes(in, M, N, K, b_layout);
         if (need < 0)
             return TG_ERR_INVALID_VALUE;
         if (workspace_bytes < need)

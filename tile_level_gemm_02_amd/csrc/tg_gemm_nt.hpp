@@ -377,10 +377,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
             for (int r = 0; r < NR; ++r)
                 if (r * NT / NR == t)
                     rd(r);
+            if constexpr (NQ > 0) {
 #pragma unroll
-            for (int q = 0; q < NQ; ++q)
-                if (q * NT / NQ == t)
-                    cp(q);
+                for (int q = 0; q < NQ; ++q)
+                    if (q * NT / NQ == t)
+                        cp(q);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };

@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "tg.h"
+#include "tg_abi.hpp"
 #include "tg_gemm_nt.hpp"
 #include "tg_gemm_skinny.hpp"
 #include "tg_kernels.hpp"
@@ -14,7 +14,7 @@ namespace tg {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0u; }
 
-inline int out_bytes(tg_dtype d) { return d == TG_F32 ? 4 : 2; }
+inline int out_bytes(int d) { return d == TG_F32 ? 4 : 2; }
 
 // Validate a dense GEMM call (A: M x K, B: K x N in `b_layout`, C: M x N).
 // Returns TG_OK and sets *empty when nothing is to be computed.
@@ -29,6 +29,8 @@ inline tg_status check_dense(int64_t M, int64_t N, int64_t K, const void* A, int
         return TG_ERR_INVALID_VALUE;
     if (c_dtype != TG_F32 && c_dtype != TG_F16 && c_dtype != TG_BF16)
         return TG_ERR_INVALID_VALUE;
+    if (!dims_fit(M, N, K, lda, ldb, ldc))
+        return TG_ERR_NOT_SUPPORTED;
     if (M == 0 || N == 0) {
         *empty = true;
         return TG_OK;
@@ -45,7 +47,7 @@ inline tg_status check_dense(int64_t M, int64_t N, int64_t K, const void* A, int
         if (!aligned16(A) || !aligned16(B) || ((lda * elem_bytes) & 15) || ((ldb * elem_bytes) & 15))
             return TG_ERR_MISALIGNED;
     }
-    if (!aligned16(C) || ((ldc * out_bytes((tg_dtype)c_dtype)) & 15))
+    if (!aligned16(C) || ((ldc * out_bytes(c_dtype)) & 15))
         return TG_ERR_MISALIGNED;
     return TG_OK;
 }
@@ -461,7 +463,7 @@ template <int E>
 int64_t dense_ws_bytes(int64_t M, int64_t N, int64_t K, int b_layout)
 {
     constexpr int CE = 16 / ElemInfo<E>::bytes;
-    if (M <= 0 || N <= 0 || K <= 0)
+    if (M <= 0 || N <= 0 || K <= 0 || !dims_fit(M, N, K))
         return 0;
     if (E != E_FP8 && M <= kSkSliceMaxM && b_layout == TG_COL_MAJOR) {  // the skinny kernel (any K)
         const int64_t blocks = skinny_blocks(M, N);

@@ -6,6 +6,9 @@
 
 #include "tg_host.hpp"
 
+namespace tg {
+int64_t ex_workspace_bytes(int in, int64_t M, int64_t N, int64_t K, int b_layout);  // tg_ex.hip
+}
 
 namespace {
 
@@ -55,10 +58,11 @@ tg_status scratch_of_current_device(hipStream_t stream, void** out)
 
 }  // namespace
 
-extern "C" tg_status tg_gemm_ex_noalloc(tg_input in, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                                        const void* B, int64_t ldb, tg_layout b_layout, float scale_a, float scale_b,
-                                        void* C, int64_t ldc, tg_dtype c_dtype, void* stream)
+extern "C" tg_status tg_gemm_ex_noalloc(tg_input in_arg, int64_t M, int64_t N, int64_t K, const void* A,
+                                        int64_t lda, const void* B, int64_t ldb, tg_layout b_layout_arg, float scale_a,
+                                        float scale_b, void* C, int64_t ldc, tg_dtype c_dtype_arg, void* stream)
 {
+    const int in = tg::abi_int(in_arg), b_layout = tg::abi_int(b_layout_arg), c_dtype = tg::abi_int(c_dtype_arg);
     if (in != TG_IN_F16 && in != TG_IN_BF16 && in != TG_IN_FP8)
         return TG_ERR_INVALID_VALUE;
     // every argument is checked before the first HIP call (the scratch set-up)
@@ -69,7 +73,7 @@ extern "C" tg_status tg_gemm_ex_noalloc(tg_input in, int64_t M, int64_t N, int64
         return chk;
     if (in == TG_IN_FP8 && (!__builtin_isfinite(scale_a) || !__builtin_isfinite(scale_b)))
         return TG_ERR_INVALID_VALUE;
-    const int64_t need = tg_gemm_ex_workspace_bytes(in, M, N, K, b_layout);
+    const int64_t need = tg::ex_workspace_bytes(in, M, N, K, b_layout);
     if (need < 0)
         return TG_ERR_INVALID_VALUE;
     if (need > kScratchBytes)

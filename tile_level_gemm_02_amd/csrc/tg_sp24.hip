@@ -17,12 +17,15 @@ bool sp24_offsets_fit(int64_t K, int64_t lda, int64_t ldv, int64_t ldm)
 
 extern "C" tg_status tg_gemm_sp24_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                        const void* Wv, int64_t ldv, const void* Wm, int64_t ldm,
-                                       void* C, int64_t ldc, tg_dtype c_dtype, void* stream)
+                                       void* C, int64_t ldc, tg_dtype c_dtype_arg, void* stream)
 {
+    const int c_dtype = tg::abi_int(c_dtype_arg);
     if (M < 0 || N < 0 || K < 0)
         return TG_ERR_INVALID_VALUE;
     if (c_dtype != TG_F32 && c_dtype != TG_F16 && c_dtype != TG_BF16)
         return TG_ERR_INVALID_VALUE;
+    if (!tg::dims_fit(M, N, K, lda, ldv, ldm) || !tg::dims_fit(ldc, 0, 0))
+        return TG_ERR_NOT_SUPPORTED;
     if (K % 64 != 0)
         return TG_ERR_NOT_SUPPORTED;
     if (M == 0 || N == 0)

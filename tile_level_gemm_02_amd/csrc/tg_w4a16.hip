@@ -29,6 +29,8 @@ tg_status check_w4(int64_t N, int64_t K, const int32_t* qweight, int64_t ldq, co
 {
     if (N < 0 || K < 0)
         return TG_ERR_INVALID_VALUE;
+    if (!tg::dims_fit(N, K, ldq, lds))
+        return TG_ERR_NOT_SUPPORTED;
     if (group_size != 128 || (K % 128) != 0 || zero_point < 0 || zero_point > 15)
         return TG_ERR_NOT_SUPPORTED;
     if (N > 0 && K > 0) {
@@ -128,7 +130,7 @@ bool launch_skinny_lds(const tg::TileArgs& a, hipStream_t s, tg_status* st)
 // scales of even stride, and 32-bit buffer offsets over a tile; 1 = no split.
 int w4s_splits(int64_t M, int64_t N, int64_t K)
 {
-    if (M <= kW4SliceMaxM || K <= 0 || K % 256 != 0)
+    if (M <= kW4SliceMaxM || N <= 0 || K <= 0 || K % 256 != 0 || !tg::dims_fit(M, N, K))
         return 1;
     const int64_t tiles = tg::n_tiles<128, 128>(M, N), G = K / 128;
     if (tiles >= 256 || tiles > tg::kSplitMaxCounters)
@@ -205,6 +207,8 @@ tg_status w4a16_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
 {
     if (M < 0)
         return TG_ERR_INVALID_VALUE;
+    if (!tg::dims_fit(M, lda, ldc))
+        return TG_ERR_NOT_SUPPORTED;
     tg_status st = check_w4(N, K, qweight, ldq, scales, lds, group_size, zero_point);
     if (st != TG_OK)
         return st;
@@ -285,6 +289,8 @@ extern "C" tg_status tg_dequant_w4(int64_t N, int64_t K, const int32_t* qweight,
         return st;
     if (N == 0 || K == 0)
         return TG_OK;
+    if (!tg::dims_fit(ldw, 0, 0))
+        return TG_ERR_NOT_SUPPORTED;
     if (W == nullptr || ldw < K)
         return TG_ERR_INVALID_VALUE;
     if (!tg::aligned16(W) || ((ldw * 2) & 15))
