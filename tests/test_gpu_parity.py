@@ -485,13 +485,13 @@ def test_w4a16_layouts(tg, case):
 # columns per workgroup for M <= 4, 32 above; a single stage per wave and
 # several);
 # other K the register kernel (eight waves split the 128-K groups: a group
-# count below, equal to and not a multiple of the wave count).  Ragged N,
-# both ends of the zero-point range.
+# count below, equal to and not a multiple of the wave count, here also at
+# 1280, 2304 and 256).  Ragged N, both ends of the zero-point range.
 @pytest.mark.parametrize("shape", [(1, 8, 128), (2, 40, 384), (7, 100, 1152), (16, 33, 256),
                                    (16, 520, 2176), (5, 64, 1024), (1, 1000, 4096),
                                    (2, 72, 2048), (3, 33, 3072), (8, 100, 1024), (9, 64, 2048),
                                    (16, 520, 1024), (16, 40, 8192), (4, 31, 5120), (3, 33, 6144),
-                                   (4, 100, 2048)],
+                                   (4, 100, 2048), (1, 300, 1280), (16, 72, 2304), (6, 8, 256)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("zp", [0, 15])
 def test_w4a16_decode(tg, shape, zp):
