@@ -776,9 +776,12 @@ def _run_sp(tg, A, vals, meta, out):
 
 
 # one tile and many, ragged M and N on both sides of the 256 tile, K of one
-# step (64) and several
+# step (64) and several; K a multiple of 128 copies the codes once per 4
+# steps (whole periods, and a last period of 2 steps at K = 128, 384, 640),
+# other K once per step (K = 64, 192, 320)
 @pytest.mark.parametrize("shape", [(1, 1, 64), (7, 9, 64), (64, 64, 128), (256, 256, 256), (300, 260, 512),
-                                   (513, 200, 1024), (1000, 1100, 192)], ids=lambda s: "x".join(map(str, s)))
+                                   (513, 200, 1024), (1000, 1100, 192), (300, 260, 384), (260, 513, 640),
+                                   (40, 300, 320)], ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 def test_sp24_small(tg, out, shape):
     M, N, K = shape
@@ -826,10 +829,13 @@ def test_random_w4a16_sp24(tg, case):
     assert ok, (r, idx)
 
 
-def test_sp24_one_hot_rows_read_the_weights(tg):
+@pytest.mark.parametrize("K", [256, 384, 320])
+def test_sp24_one_hot_rows_read_the_weights(tg, K):
     """A row that is one-hot at k gives C[., n] = W[n][k] exactly: every kept value
-    lands at its coded position and every other position contributes zero."""
-    N, K = 300, 256
+    lands at its coded position and every other position contributes zero
+    (codes per 4 steps with whole periods and a 2-step last period, and codes
+    per step)."""
+    N = 300
     _, v, m = _sp_inputs(1, N, K, seed=61)
     ks = list(range(0, K, 3)) + [K - 1]
     A = torch.zeros((len(ks), K), dtype=torch.bfloat16)

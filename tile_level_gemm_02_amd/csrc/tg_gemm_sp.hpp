@@ -21,6 +21,16 @@
 // of codes (8 B per row), all copied straight into LDS.  A ring of 3 such
 // stages with one barrier per step: the copies of step k+3 are issued, spread
 // between the MFMAs, right after the barrier that frees step k's stage.
+//
+// The copies bound this kernel (a step moves ≈50 KB into the compute unit
+// for 1056 cycles of sparse MFMAs), and each copy instruction costs the
+// address unit about the same whether it moves 1 KiB or the 256 bytes of a
+// step's codes.  So with CP4 (K a multiple of 128) the codes are copied once
+// per 4 steps, 16 bytes per lane (a row's codes of two steps), into a ring of
+// two 8 KiB periods outside the stages: 25 copy instructions per wave per 4
+// steps instead of 28.  Period layout: wave w's copy holds rows 32w .. 32w+31
+// as [step pair][row][16 bytes], so a fragment read (32 consecutive rows of
+// one step) touches 32 different banks.
 #pragma once
 
 #include "tg_gemm_nt.hpp"
@@ -54,18 +64,21 @@ __device__ __forceinline__ void load_lds_256_at(i32x4_t r, uint32_t dst, uint32_
 
 constexpr int kSpThreads = 512;
 
-template <int O>
+template <int O, bool CP4>
 __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
 {
     constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NW = WM * WN;
     constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 4 x 2 blocks of 32 x 32 per wave
     constexpr int KE = 64;                              // dense k per step
-    constexpr int AB = BM * 128, VB = BN * 64, MB = BN * 8;
+    constexpr int AB = BM * 128, VB = BN * 64, MB = CP4 ? 0 : BN * 8;
     constexpr int STAGE = AB + VB + MB;
     constexpr int NS = 3;
+    constexpr int CPB = BN * 32;               // codes of a 4-step period (CP4)
+    constexpr int CODES = NS * STAGE;          // offset of the two code periods (CP4)
+    constexpr int BYTES = NS * STAGE + (CP4 ? 2 * CPB : 0);
     constexpr int PER = 4 + 2 + 1;  // copy instructions per wave per step: A rows, values, codes
-    static_assert(NS * STAGE <= 160 * 1024, "LDS");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+    static_assert(BYTES <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[BYTES];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -98,6 +111,9 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
     const uint32_t va0 = arow * ldab + ach0 * 16u, va1 = arow * ldab + ach1 * 16u;
     const uint32_t vv = vrow * ldvb + vch * 16u;
     const uint32_t vm = mrow * ldmb + (lane % 2u) * 4u;
+    // CP4: lane l copies the codes of row 32w + l%32 for step pair l/32 of a period
+    const uint32_t crow = wave * 32u + lane % 32u, cpair = lane / 32u;
+    const uint32_t vc = crow * ldmb + cpair * 16u;
 
     // copy instruction q (0 .. PER-1) of step kt into the stage at byte offset `so`
     auto copy = [&](auto edge, int64_t kt, uint32_t so, int q) __attribute__((always_inline)) {
@@ -115,13 +131,20 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
                 v |= (int32_t)(vrow + 16u * j) < rows_w ? 0u : kOutOfRange;
             load_lds_1k_at(rv, base + AB + wave * 2048u + j * 1024u, v,
                            (uint32_t)kt * 64u + (uint32_t)(16 * j) * ldvb);
-        } else {
+        } else if constexpr (!CP4) {
             uint32_t v = vm | past;
             if constexpr (decltype(edge)::value)
                 v |= (int32_t)mrow < rows_w ? 0u : kOutOfRange;
             load_lds_256_at(rm, base + AB + VB + wave * 256u, v, (uint32_t)kt * 8u);
+        } else if ((kt & 3) == 0) {  // CP4: the codes of steps kt .. kt+3 (pairs past K read zeros)
+            uint32_t v = vc | (kt + 2 * (int64_t)cpair < KT ? 0u : kOutOfRange);
+            if constexpr (decltype(edge)::value)
+                v |= (int32_t)crow < rows_w ? 0u : kOutOfRange;
+            load_lds_1k_at(rm, lds0 + CODES + (uint32_t)((kt >> 2) & 1) * CPB + wave * 1024u, v, (uint32_t)kt * 8u);
         }
     };
+    // copy instructions in the batch of step kt (the wait counts below)
+    auto batch = [&](int64_t kt) __attribute__((always_inline)) { return CP4 && (kt & 3) != 0 ? PER - 1 : PER; };
 
     // ---- fragments.  Every row a lane reads has the same swizzle.
     const uint32_t wm = wave / WN, wn = wave % WN;
@@ -131,16 +154,24 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
     const uint32_t w_row0 = wn * (BN / WN) + lrow;
     u32x4 fx[2][TM][2], fw[2][TN];
     uint32_t fi[2][TN];
-    // fragment read r (0 .. TM+TN-1) of sub-step s from the stage at byte
-    // offset `so` into slot `slot`, numbered in the order the MFMAs consume
-    // them: A block 0, every W block (values and codes), A blocks 1 .. TM-1
-    auto read_frag = [&](uint32_t so, int s, int slot, int r) __attribute__((always_inline)) {
+    // fragment read r (0 .. TM+TN-1) of sub-step s of step kt (its stage at
+    // byte offset `so`) into slot `slot`, numbered in the order the MFMAs
+    // consume them: A block 0, every W block (values and codes), A blocks
+    // 1 .. TM-1
+    auto read_frag = [&](uint32_t so, int64_t kt, int s, int slot, int r) __attribute__((always_inline)) {
         const uint8_t* st = lds + so;
         if (r >= 1 && r <= TN) {
             const int j = r - 1;
             const uint32_t row = w_row0 + j * 32;
             fw[slot][j] = lds128(st, AB + row * 64u + ((((uint32_t)(2 * s) + h) ^ swv) << 4));
-            fi[slot][j] = *(const uint16_t*)(st + AB + VB + row * 8u + 4u * s + 2u * h);
+            if constexpr (CP4) {
+                const uint32_t t = (uint32_t)kt & 3u;
+                const uint32_t off = CODES + (uint32_t)((kt >> 2) & 1) * CPB + (row / 32u) * 1024u + (t >> 1) * 512u +
+                                     (row % 32u) * 16u + (t & 1u) * 8u;
+                fi[slot][j] = *(const uint16_t*)(lds + off + 4u * s + 2u * h);
+            } else {
+                fi[slot][j] = *(const uint16_t*)(st + AB + VB + row * 8u + 4u * s + 2u * h);
+            }
         } else {
             const int i = r == 0 ? 0 : r - TN;
             const uint32_t row = a_row0 + i * 32 * 128;
@@ -190,14 +221,17 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
     // frees step kt's stage, into which step kt+3 is copied during the second
     // sub-step while step kt+1's first fragments are read.
     auto step = [&](auto edge, int64_t kt, uint32_t cur, uint32_t nxt) __attribute__((always_inline)) {
-        substep(0, [&](int r) __attribute__((always_inline)) { read_frag(cur, 1, 1, r); }, nothing,
+        substep(0, [&](int r) __attribute__((always_inline)) { read_frag(cur, kt, 1, 1, r); }, nothing,
                 std::integral_constant<int, 0>{});
         __builtin_amdgcn_sched_barrier(0);
-        wait_copies<PER>();
+        if (batch(kt + 2) == PER)  // step kt+1 landed (step kt+2 may be in flight)
+            wait_copies<PER>();
+        else
+            wait_copies<PER - 1>();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         // (the reads of step kt+1 after the last step are stale and unused)
-        substep(1, [&](int r) __attribute__((always_inline)) { read_frag(nxt, 0, 0, r); },
+        substep(1, [&](int r) __attribute__((always_inline)) { read_frag(nxt, kt + 1, 0, 0, r); },
                 [&](int q) __attribute__((always_inline)) { copy(edge, kt + NS, cur, q); },
                 std::integral_constant<int, PER>{});
     };
@@ -207,11 +241,12 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
 #pragma unroll
             for (int q = 0; q < PER; ++q)
                 copy(edge, st, (uint32_t)(st * STAGE), q);
-        wait_copies<(NS - 1) * PER>();  // step 0 landed
+        static_assert(NS == 3, "the prologue wait counts steps 1 and 2");
+        wait_copies<CP4 ? 2 * (PER - 1) : 2 * PER>();  // step 0 landed (steps 1, 2 may be in flight)
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < NR; ++r)
-            read_frag(0, 0, 0, r);
+            read_frag(0, 0, 0, 0, r);
         uint32_t cur = 0;  // byte offset of step kt's stage
         for (int64_t kt = 0; kt < KT; ++kt) {
             const uint32_t nxt = cur == (NS - 1) * STAGE ? 0u : cur + STAGE;

@@ -13,6 +13,23 @@ bool sp24_offsets_fit(int64_t K, int64_t lda, int64_t ldv, int64_t ldm)
     return 256 * lda * 2 + K * 2 < lim && 256 * ldv * 2 + K < lim && 256 * ldm + K / 8 < lim;
 }
 
+template <bool CP4>
+tg_status launch_sp24(const tg::SpArgs& a, int c_dtype, int64_t tiles, hipStream_t s)
+{
+    switch (c_dtype) {
+    case TG_F32:
+        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_F32, CP4>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
+        break;
+    case TG_F16:
+        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_F16, CP4>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
+        break;
+    default:
+        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_BF16, CP4>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
+        break;
+    }
+    return tg::launched();
+}
+
 }  // namespace
 
 extern "C" tg_status tg_gemm_sp24_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -50,16 +67,8 @@ extern "C" tg_status tg_gemm_sp24_bf16(int64_t M, int64_t N, int64_t K, const vo
     if (tiles > 0x7FFFFFFF)
         return TG_ERR_NOT_SUPPORTED;
     hipStream_t s = (hipStream_t)stream;
-    switch (c_dtype) {
-    case TG_F32:
-        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_F32>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
-        break;
-    case TG_F16:
-        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_F16>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
-        break;
-    default:
-        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_BF16>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
-        break;
-    }
-    return tg::launched();
+    // codes copied once per 4 K steps where K is whole pairs of steps
+    if (K % 128 == 0)
+        return launch_sp24<true>(a, c_dtype, tiles, s);
+    return launch_sp24<false>(a, c_dtype, tiles, s);
 }
