@@ -464,29 +464,73 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         if (!splitk_last(p.counters + (size_t)tile * NW + wave, S, lane))
             return;
         // the S partial shares in split order: acc = p_0, then acc += p_q
-        // for q = 1 .. S-1.  This wave's own share p_ks is already in acc
-        // when ks == 0, else it is read back from its slot like the others.
-        // Loads go out in batches of two accumulator blocks (8 x 16 bytes
-        // per lane) ahead of their adds: one wait per batch, not per load.
-        constexpr int NBLK = TM * TN, BB = NBLK >= 2 ? 2 : 1;
-        for (uint32_t q = ks == 0u ? 1u : 0u; q < S; ++q) {
-            const float* src = slot(q);
+        // for q = 1 .. S-1.  Up to 4 accumulator blocks per wave (the 64 and
+        // 128 tiles), this wave's own share p_ks is taken from the
+        // accumulator itself (the bits it stored) and the other shares are
+        // loaded whole, several at a time up to 64 floats per lane, all of a
+        // batch's loads ahead of its adds.  With more blocks (the 256 tile,
+        // which the planner never splits) the own share is read back like
+        // the others, two blocks at a time, to keep the registers in bounds.
+        constexpr int NBLK = TM * TN;
+        if constexpr (NBLK <= 4) {
+            constexpr int QB = 4 / NBLK;  // shares per batch
+            f32x4 own[NBLK][4];
 #pragma unroll
-            for (int b0 = 0; b0 < NBLK; b0 += BB) {
-                f32x4 v[BB][4];
+            for (int b = 0; b < NBLK; ++b)
 #pragma unroll
-                for (int bb = 0; bb < BB; ++bb)
+                for (int g = 0; g < 4; ++g)
+                    own[b][g] = f32x4{acc[b / TN][b % TN][4 * g], acc[b / TN][b % TN][4 * g + 1],
+                                      acc[b / TN][b % TN][4 * g + 2], acc[b / TN][b % TN][4 * g + 3]};
+            for (uint32_t q0 = 0; q0 < S; q0 += QB) {
+                f32x4 v[QB][NBLK][4];
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        v[bb][g] = splitk_load(src, b0 + bb, g, lane);
+                for (int qq = 0; qq < QB; ++qq) {
+                    const uint32_t q = q0 + (uint32_t)qq;
+                    if (q < S && q != ks)
 #pragma unroll
-                for (int bb = 0; bb < BB; ++bb) {
-                    const int i = (b0 + bb) / TN, j = (b0 + bb) % TN;
+                        for (int b = 0; b < NBLK; ++b)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
+                            for (int g = 0; g < 4; ++g)
+                                v[qq][b][g] = splitk_load(slot(q), b, g, lane);
+                }
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[i][j][4 * g + e] = q == 0u ? v[bb][g][e] : acc[i][j][4 * g + e] + v[bb][g][e];
+                for (int qq = 0; qq < QB; ++qq) {
+                    const uint32_t q = q0 + (uint32_t)qq;
+                    if (q < S) {
+#pragma unroll
+                        for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                const f32x4 x = q == ks ? own[b][g] : v[qq][b][g];
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    acc[b / TN][b % TN][4 * g + e] =
+                                        q == 0u ? x[e] : acc[b / TN][b % TN][4 * g + e] + x[e];
+                            }
+                    }
+                }
+            }
+        } else {
+            constexpr int BB = 2;
+            for (uint32_t q = ks == 0u ? 1u : 0u; q < S; ++q) {
+                const float* src = slot(q);
+#pragma unroll
+                for (int b0 = 0; b0 < NBLK; b0 += BB) {
+                    f32x4 v[BB][4];
+#pragma unroll
+                    for (int bb = 0; bb < BB; ++bb)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            v[bb][g] = splitk_load(src, b0 + bb, g, lane);
+#pragma unroll
+                    for (int bb = 0; bb < BB; ++bb) {
+                        const int i = (b0 + bb) / TN, j = (b0 + bb) % TN;
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                acc[i][j][4 * g + e] = q == 0u ? v[bb][g][e] : acc[i][j][4 * g + e] + v[bb][g][e];
+                    }
                 }
             }
         }

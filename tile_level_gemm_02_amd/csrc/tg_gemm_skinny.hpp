@@ -196,14 +196,32 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
         if constexpr (SPLIT == 2) {
             // this workgroup's partial tile into its slot (1 KiB: one value
             // quadruple per lane), count in; the last of the gridDim.y
-            // arrivals re-reads all of them and adds them in split order
+            // arrivals adds them in split order, its own from registers (the
+            // bits it stored) and the others loaded 8 at a time, all of a
+            // batch's loads ahead of its adds
             float* const slot0 = p.partials + (size_t)blockIdx.x * gridDim.y * 256;
             splitk_store(slot0 + blockIdx.y * 256, 0, 0, lane, sum);
             if (!splitk_last(p.counters + blockIdx.x, gridDim.y, lane))
                 return;
-            sum = splitk_load(slot0, 0, 0, lane);
-            for (uint32_t q = 1; q < gridDim.y; ++q)
-                sum += splitk_load(slot0 + q * 256, 0, 0, lane);
+            const f32x4 own = sum;
+            const uint32_t S = gridDim.y, me = blockIdx.y;
+            for (uint32_t q0 = 0; q0 < S; q0 += 8) {
+                f32x4 v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t q = q0 + (uint32_t)j;
+                    if (q < S && q != me)
+                        v[j] = splitk_load(slot0 + q * 256, 0, 0, lane);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t q = q0 + (uint32_t)j;
+                    if (q < S) {
+                        const f32x4 x = q == me ? own : v[j];
+                        sum = q == 0u ? x : sum + x;
+                    }
+                }
+            }
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {

@@ -321,16 +321,31 @@ __global__ __launch_bounds__(kW4sThreads) __attribute__((amdgpu_waves_per_eu(2, 
         asm volatile("" ::: "memory");  // no load of a partial is moved above the count
         if (grp == 0) {
             // acc = p_0 + p_1 + ... in split order; this workgroup's own share
-            // is already in acc when ks == 0, else it is read back like the others
-            // (all of a partial's loads go out before its adds: one wait per partial)
-            for (uint32_t q = ks == 0u ? 1u : 0u; q < S; ++q) {
-                const float* src = slot(q);
+            // p_ks is the accumulator itself (the bits it stored), only the
+            // others are loaded (all of a partial's loads go out before its
+            // adds: one wait per partial)
+            f32x4 own[TM][4];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    own[i][g] = f32x4{acc[i][4 * g], acc[i][4 * g + 1], acc[i][4 * g + 2], acc[i][4 * g + 3]};
+            for (uint32_t q = 0; q < S; ++q) {
                 f32x4 v[TM][4];
+                if (q != ks) {
+                    const float* src = slot(q);
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+                    for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        v[i][g] = splitk_load(src, i, g, lane);
+                        for (int g = 0; g < 4; ++g)
+                            v[i][g] = splitk_load(src, i, g, lane);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            v[i][g] = own[i][g];
+                }
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
