@@ -77,3 +77,35 @@ def test_noalloc_repeats_bitwise(tg):
     C1, _, _, _ = _pair(tg, "bf16", "bf16", 256, 8192, 8192, seed=100)
     C3, _, _, _ = _pair(tg, "bf16", "bf16", 256, 8192, 8192, seed=100)
     assert torch.equal(C1.view(torch.int16), C3.view(torch.int16))
+
+
+def test_noalloc_under_graph_capture(tg):
+    """The use the entry point is for: a call captured in a HIP graph (nothing
+    allocated inside the capture) and replayed, with eager work and
+    synchronizations between the replays; each replay, on new contents of A,
+    equals an eager call on the same inputs bit for bit."""
+    M, N, K = 256, 8192, 8192
+    _, B, _, _ = _inputs("bf16", M, N, K, seed=300)
+    dB = B.cuda()
+    dA = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Ce = torch.empty_like(C)
+    dA.copy_(synth.normal((M, K), 301).to(torch.bfloat16))
+    tg.tg_gemm_ex_noalloc(dA, dB, Ce, b_layout="col")  # eager first call: the scratch is set up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tg.tg_gemm_ex_noalloc(dA, dB, C, b_layout="col")
+    torch.cuda.synchronize()
+    for rep in range(3):
+        print(f"graph replay {rep}", flush=True)
+        dA.copy_(synth.normal((M, K), 302 + rep).to(torch.bfloat16))
+        tg.tg_gemm_ex_noalloc(dA, dB, Ce, b_layout="col")  # eager, on the same inputs
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C.view(torch.int16), Ce.view(torch.int16)), f"replay {rep} differs from the eager call"
+    A_last = dA.cpu()
+    cref, S = oracle.gemm(FMT["bf16"], A_last, B, oracle.B_NK)
+    ok, r, idx = ochk.check(C.float().cpu().double().numpy(), cref, S, K, "bf16")
+    assert ok, (r, idx)
