@@ -111,12 +111,23 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
         va[i] = (int64_t)r < M ? r * (uint32_t)p.lda * 2u + sk_swz(r, lane % 8u) * 16u : kOutOfRange;
     }
     const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(lds)) + wave * (RING * SLOT);
+    // B rows read by this workgroup alone (one slice) stream with the
+    // non-temporal hint; with several slices the later ones read them from L2
+    // (measured: M = 16 29.2 -> 28.0 us per flushed launch at N = K = 8192;
+    // M = 24 and 32 lose 3.5-6 us with it)
+    const bool b_once = S == 1;
     auto issue = [&](int64_t st, uint32_t slot) __attribute__((always_inline)) {
         const uint32_t past = st < nst ? 0u : kOutOfRange;
         const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((s0 + st) * kSkRow));
+        if (b_once) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            load_lds_1k_at(rb, slot + i * 1024, vb[i] | past, soff);
+            for (int i = 0; i < 2; ++i)
+                load_lds_1k_nt_at(rb, slot + i * 1024, vb[i] | past, soff);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                load_lds_1k_at(rb, slot + i * 1024, vb[i] | past, soff);
+        }
 #pragma unroll
         for (int i = 0; i < AI; ++i)
             load_lds_1k_at(ra, slot + kSkCols * kSkRow + i * 1024, va[i] | past, soff);
