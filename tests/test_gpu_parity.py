@@ -214,12 +214,14 @@ def test_skinny_outputs_strided(tg, out, M, K):
 # when N and K are multiples of 8: ragged tiles on every side, K tails of one
 # chunk and of several, padded leading dimensions, all outputs; and a large
 # case on sampled rows.
-# Batches of 17 .. 32 rows against a K-contiguous B: the skinny kernel in
-# 16-row slices (column blocks padded to a multiple of 8 when there are
-# several slices), ragged N, K tails, and narrow N with fp32 output (the
-# slices split K over workgroups too); 33 .. 64 rows: the tile kernel
+# Batches of 17 .. 48 rows against a K-contiguous B: the skinny kernel in
+# 16-row slices with 32 columns per workgroup (column blocks padded to a
+# multiple of 8), ragged N (not a multiple of 32), K tails, and narrow N with
+# fp32 output (the slices split K over workgroups too); 49 .. 64 rows: the
+# tile kernel
 @pytest.mark.parametrize("shape", [(17, 200, 1000), (24, 1000, 4096), (32, 264, 4101), (33, 520, 136),
-                                   (48, 2056, 2048), (64, 88, 520), (64, 1024, 8192)],
+                                   (40, 72, 4101), (48, 2056, 2048), (48, 100, 8192), (49, 264, 520),
+                                   (64, 88, 520), (64, 1024, 8192)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("dt", ["f16", "bf16"])

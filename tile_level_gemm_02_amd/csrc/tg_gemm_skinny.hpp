@@ -6,9 +6,9 @@
 // README's GEMM example (section "Example of GEMM"), where warpgroups split
 // K and all-reduce on chip.
 //
-// Each workgroup owns 16 columns (B rows).  Each wave streams its K range
-// through a private LDS ring of RING slots with direct-to-LDS copies; a slot
-// holds one stage of 64 k: 128 bytes of each of the 16 B rows and of the A
+// Each workgroup owns 16 or 32 columns (B rows).  Each wave streams its K
+// range through a private LDS ring of RING slots with direct-to-LDS copies; a
+// slot holds one stage of 64 k: 128 bytes of each of the B rows and of the A
 // rows.  One copy instruction fetches 8 rows x 128 bytes -- whole cache lines
 // -- which the memory system streams faster than the 16 rows x 64 bytes a
 // lane-per-operand register load would fetch.  Chunks are XOR-swizzled by
@@ -30,13 +30,12 @@
 
 namespace tg {
 
-constexpr int kSkCols = 16;   // columns (B rows) per workgroup
 constexpr int kSkKE = 64;     // k per stage
 constexpr int kSkRow = 128;   // bytes per staged row (16-bit elements)
 
-// Slot bytes: the 16 B rows, then 8*AI A rows (AI copy instructions).
-template <int AI> struct SkinnySlot {
-    static constexpr int BYTES = (kSkCols + 8 * AI) * kSkRow;
+// Slot bytes: the 16*CG B rows, then 8*AI A rows (AI copy instructions).
+template <int AI, int CG> struct SkinnySlot {
+    static constexpr int BYTES = (16 * CG + 8 * AI) * kSkRow;
 };
 
 // physical 16-byte chunk of logical chunk c of staged row r: two rows share
@@ -55,17 +54,23 @@ __device__ __forceinline__ uint32_t sk_swz(uint32_t r, uint32_t c)
 //   SPLIT = 2: each stores its partial tile in a workspace slot and counts
 //              in; the last to arrive adds the partials in split order (a
 //              fixed order) and stores C, of any output type (splitk_last).
-template <int E, int O, int WAVES, int AI, int RING, int SPLIT = 0>
+//
+// CG: 16-column groups per workgroup (16*CG columns).  Every workgroup
+// copies its slice's A rows over all of K, so with CG = 2 the A bytes the
+// compute units copy halve, for half the workgroups.
+template <int E, int O, int WAVES, int AI, int RING, int SPLIT = 0, int CG = 1>
 __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
 {
     typedef typename OutInfo<O>::T OutT;
     static_assert(E == E_F16 || E == E_BF16, "16-bit inputs");
     static_assert(SPLIT != 1 || O == O_F32, "partial tiles are added in fp32");
-    constexpr int SLOT = SkinnySlot<AI>::BYTES;
-    constexpr int PER = 2 + AI;  // copy instructions per stage
+    constexpr int SLOT = SkinnySlot<AI, CG>::BYTES;
+    constexpr int COLS = 16 * CG;          // columns (B rows) per workgroup
+    constexpr int BI = COLS / 8;           // B copy instructions per stage
+    constexpr int PER = BI + AI;           // copy instructions per stage
     constexpr int ZERO = WAVES * RING * SLOT;  // 16 zero bytes: A rows past 8*AI
     static_assert(AI >= 1 && AI <= 2 && RING >= 2 && (RING - 1) * PER <= 63, "copy ring");
-    static_assert(ZERO + 16 <= 160 * 1024 && WAVES * 4 * 64 * 4 <= ZERO, "LDS");
+    static_assert(ZERO + 16 <= 160 * 1024 && WAVES * CG * 4 * 64 * 4 <= ZERO, "LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[ZERO + 16];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
@@ -78,7 +83,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
     const int64_t S = (p.M + 15) / 16;
     const int64_t grp8 = (int64_t)blockIdx.x / (8 * S), rem = (int64_t)blockIdx.x % (8 * S);
     const int64_t slice = rem / 8;
-    const int64_t n0 = (grp8 * 8 + rem % 8) * kSkCols;
+    const int64_t n0 = (grp8 * 8 + rem % 8) * COLS;
     if (n0 >= N)
         return;  // padding of the last group of eight column blocks (whole workgroup)
     const int64_t M = p.M - 16 * slice < 16 ? p.M - 16 * slice : 16;  // rows of this slice
@@ -99,9 +104,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
     // plus the stage offsets the ring forms, stays below 2^31.
     const i32x4_t ra = make_rsrc(Ab);
     const i32x4_t rb = make_rsrc(p.B + n0 * p.ldb * 2);
-    uint32_t vb[2], va[AI];
+    uint32_t vb[BI], va[AI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < BI; ++i) {
         const uint32_t r = 8u * i + lane / 8u;
         vb[i] = n0 + r < N ? r * (uint32_t)p.ldb * 2u + sk_swz(r, lane % 8u) * 16u : kOutOfRange;
     }
@@ -121,20 +126,23 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
         const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((s0 + st) * kSkRow));
         if (b_once) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < BI; ++i)
                 load_lds_1k_nt_at(rb, slot + i * 1024, vb[i] | past, soff);
         } else {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < BI; ++i)
                 load_lds_1k_at(rb, slot + i * 1024, vb[i] | past, soff);
         }
 #pragma unroll
         for (int i = 0; i < AI; ++i)
-            load_lds_1k_at(ra, slot + kSkCols * kSkRow + i * 1024, va[i] | past, soff);
+            load_lds_1k_at(ra, slot + COLS * kSkRow + i * 1024, va[i] | past, soff);
     };
 
-    // two accumulators (the two 32-k halves of a stage)
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // two accumulators per column group (the two 32-k halves of a stage)
+    f32x4 acc[CG][2];
+#pragma unroll
+    for (int g = 0; g < CG; ++g)
+        acc[g][0] = acc[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t c16 = lane & 15u, h = lane >> 4;
     const bool arow = c16 < 8u * AI;  // this lane's A row is held in the slot
     const uint32_t lbase = wave * (RING * SLOT);
@@ -143,9 +151,13 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const uint32_t c = 4u * s + h;
-            const u32x4 a = lds128(lds, arow ? slot + (kSkCols + c16) * kSkRow + (sk_swz(c16, c) << 4) : (uint32_t)ZERO);
-            const u32x4 b = lds128(lds, slot + c16 * kSkRow + (sk_swz(c16, c) << 4));
-            acc[s] = Mfma16<E>::run(b, a, acc[s]);
+            const u32x4 a = lds128(lds, arow ? slot + (COLS + c16) * kSkRow + (sk_swz(c16, c) << 4) : (uint32_t)ZERO);
+#pragma unroll
+            for (int g = 0; g < CG; ++g) {
+                // (rows 16g + c16 share sk_swz with row c16)
+                const u32x4 b = lds128(lds, slot + (16u * g + c16) * kSkRow + (sk_swz(c16, c) << 4));
+                acc[g][s] = Mfma16<E>::run(b, a, acc[g][s]);
+            }
         }
     };
 
@@ -177,32 +189,40 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
                 const uint8_t* src = Ab + ((int64_t)c16 * p.lda + k) * 2;
                 a = (k + 8 <= K) ? ldg128(src) : load_chunk_partial<2>(src, K - k);
             }
-            if (n0 + c16 < N && k < K) {
-                const uint8_t* src = p.B + ((n0 + c16) * p.ldb + k) * 2;
-                b = (k + 8 <= K) ? ldg128(src) : load_chunk_partial<2>(src, K - k);
+#pragma unroll
+            for (int g = 0; g < CG; ++g) {
+                const int64_t n = n0 + 16 * g + c16;
+                b = u32x4{0u, 0u, 0u, 0u};
+                if (n < N && k < K) {
+                    const uint8_t* src = p.B + (n * p.ldb + k) * 2;
+                    b = (k + 8 <= K) ? ldg128(src) : load_chunk_partial<2>(src, K - k);
+                }
+                acc[g][0] = Mfma16<E>::run(b, a, acc[g][0]);
             }
-            acc[0] = Mfma16<E>::run(b, a, acc[0]);
         }
     }
     mfma_drain();
 
-    // partial tiles: value v of lane l is row l%16, column 4*(l/16) + v
+    // partial tiles: value v of lane l is row l%16, column 16g + 4*(l/16) + v
     __syncthreads();
-    float* red = (float*)lds;  // [wave][v][lane]
+    float* red = (float*)lds;  // [wave][group][v][lane]
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-        red[(wave * 4 + v) * 64 + lane] = acc[0][v] + acc[1][v];
+    for (int g = 0; g < CG; ++g)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            red[((wave * CG + g) * 4 + v) * 64 + lane] = acc[g][0][v] + acc[g][1][v];
     __syncthreads();
-    if (wave == 0) {  // sum over the K split, in wave order
+    if (wave < (uint32_t)CG) {  // wave g sums column group g over the K split, in wave order
+        const uint32_t g = wave;
         OutT* C = (OutT*)p.C + 16 * slice * p.ldc;
         const int64_t r = c16;
         f32x4 sum;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            sum[v] = red[v * 64 + lane];
+            sum[v] = red[(g * 4 + v) * 64 + lane];
 #pragma unroll
             for (int w = 1; w < WAVES; ++w)
-                sum[v] += red[(w * 4 + v) * 64 + lane];
+                sum[v] += red[((w * CG + g) * 4 + v) * 64 + lane];
         }
         if constexpr (SPLIT == 2) {
             // this workgroup's partial tile into its slot (1 KiB: one value
@@ -210,9 +230,10 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
             // arrivals adds them in split order, its own from registers (the
             // bits it stored) and the others loaded 8 at a time, all of a
             // batch's loads ahead of its adds
-            float* const slot0 = p.partials + (size_t)blockIdx.x * gridDim.y * 256;
+            // (per column group: slots [block][group][split], counter [block][group])
+            float* const slot0 = p.partials + ((size_t)blockIdx.x * CG + g) * gridDim.y * 256;
             splitk_store(slot0 + blockIdx.y * 256, 0, 0, lane, sum);
-            if (!splitk_last(p.counters + blockIdx.x, gridDim.y, lane))
+            if (!splitk_last(p.counters + (size_t)blockIdx.x * CG + g, gridDim.y, lane))
                 return;
             const f32x4 own = sum;
             const uint32_t S = gridDim.y, me = blockIdx.y;
@@ -236,7 +257,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int64_t col = n0 + 4 * h + v;
+            const int64_t col = n0 + 16 * g + 4 * h + v;
             if (r < M && col < N) {
                 if constexpr (SPLIT == 1)
                     atomicAdd((float*)C + r * p.ldc + col, sum[v]);
@@ -249,13 +270,13 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_gemm(SkinnyArgs p)
 
 // Whether every buffer offset of skinny_gemm stays below the descriptor's
 // range: the largest row offset of A (16 rows) and of a column block of B
-// (16 rows), plus the stage offsets the ring forms (up to RING stages past
-// the end of K).
-inline bool skinny_offsets_fit(int64_t K, int64_t lda, int64_t ldb, int ring)
+// (16 * cg rows), plus the stage offsets the ring forms (up to RING stages
+// past the end of K).
+inline bool skinny_offsets_fit(int64_t K, int64_t lda, int64_t ldb, int ring, int cg)
 {
     const int64_t span = K * 2 + (int64_t)ring * kSkRow + kSkRow;
     const int64_t lim = (int64_t)kNumRecords;
-    return 16 * lda * 2 + span < lim && 16 * ldb * 2 + span < lim;
+    return 16 * lda * 2 + span < lim && 16 * cg * ldb * 2 + span < lim;
 }
 
 }  // namespace tg

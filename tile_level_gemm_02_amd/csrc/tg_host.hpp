@@ -321,48 +321,90 @@ inline int skinny_split(int64_t blocks, int64_t K)
     return split > 1 ? (int)split : 1;
 }
 
-template <int E, int O, int AI, int SPLIT>
+// 16-column groups per skinny workgroup: two when M takes several 16-row
+// slices (each slice's workgroups copy its A rows over all of K, so wider
+// workgroups halve those bytes: bf16 N = K = 8192, flushed, M = 24 40.4 ->
+// 36.5 us and M = 32 42.5 -> 38.3 us), one for a single slice (M = 16:
+// 28.0 us against 28.3; two per CU of the narrower workgroups keep more
+// copies in flight).
+inline int skinny_cg(int64_t M) { return M > 16 ? 2 : 1; }
+
+template <int E, int O, int AI, int SPLIT, int CG>
 void launch_skinny_ai(const SkinnyArgs& sa, int64_t blocks, int split, hipStream_t s)
 {
     typedef SkinnyCfg G;
-    hipLaunchKernelGGL((skinny_gemm<E, O, G::WAVES, AI, G::RING, SPLIT>), dim3((uint32_t)blocks, (uint32_t)split),
+    hipLaunchKernelGGL((skinny_gemm<E, O, G::WAVES, AI, G::RING, SPLIT, CG>), dim3((uint32_t)blocks, (uint32_t)split),
                        dim3(64 * G::WAVES), 0, s, sa);
 }
 
-// A rows are copied 8 at a time: one copy instruction for M <= 8, two above.
+// A rows are copied 8 at a time: one copy instruction for M <= 8, two above
+// (16-row slices above 16).
 template <int E, int O, int SPLIT = 0>
 void launch_skinny(const SkinnyArgs& sa, int64_t blocks, int split, hipStream_t s)
 {
     if (sa.M <= 8)
-        launch_skinny_ai<E, O, 1, SPLIT>(sa, blocks, split, s);
+        launch_skinny_ai<E, O, 1, SPLIT, 1>(sa, blocks, split, s);
+    else if (skinny_cg(sa.M) == 1)
+        launch_skinny_ai<E, O, 2, SPLIT, 1>(sa, blocks, split, s);
     else
-        launch_skinny_ai<E, O, 2, SPLIT>(sa, blocks, split, s);
+        launch_skinny_ai<E, O, 2, SPLIT, 2>(sa, blocks, split, s);
 }
 
 // Workspace of the skinny kernel's split through partial tiles: the
-// counters (one per workgroup column), then a 1 KiB partial tile per
-// workgroup; 0 where the counters would not fit their region.
-inline int64_t skinny_ws_bytes(int64_t blocks, int split)
+// counters (one per workgroup column and 16-column group), then a 1 KiB
+// partial tile per workgroup and group; 0 where the counters would not fit
+// their region.
+inline int64_t skinny_ws_bytes(int64_t M, int64_t blocks, int split)
 {
-    if (split <= 1 || blocks > kSplitMaxCounters)
+    const int64_t groups = skinny_cg(M);
+    if (split <= 1 || blocks * groups > kSplitMaxCounters)
         return 0;
-    return kSplitCounterBytes + blocks * split * 1024;
+    return kSplitCounterBytes + blocks * groups * split * 1024;
 }
 
-// Workgroup columns of the skinny kernel: one per 16-column block and 16-row
-// slice of M; with several slices the column blocks are padded to a
-// multiple of 8.
+// Workgroup columns of the skinny kernel: one per column block (16 *
+// skinny_cg(M) columns) and 16-row slice of M; with several slices the
+// column blocks are padded to a multiple of 8.
 inline int64_t skinny_blocks(int64_t M, int64_t N)
 {
-    const int64_t nblk = (N + kSkCols - 1) / kSkCols, slices = (M + 15) / 16;
+    const int64_t cols = 16 * skinny_cg(M);
+    const int64_t nblk = (N + cols - 1) / cols, slices = (M + 15) / 16;
     return slices == 1 ? nblk : (nblk + 7) / 8 * 8 * slices;
 }
 
 // Batches up to this many rows against a K-contiguous B take the skinny
 // kernel, in 16-row slices (each slice re-reads B, mostly from L2).  At
-// N = K = 8192 (bf16, flushed): 17 rows 37 us and 32 rows 43 against 46 for
-// the 64-tile NT kernel; from 40 rows on (53 us) the tile kernel is faster.
-constexpr int64_t kSkSliceMaxM = 32;
+// N = K = 8192 (bf16, flushed, 32 columns per workgroup): 17 rows 34 us,
+// 32 rows 38, 33 rows 47 and 48 rows 50, against 53 for the tile kernel
+// (without a workspace: no K split).  Where the NT kernel splits K over
+// workgroups through a caller workspace it is faster from 33 rows on (36 us
+// for 33-64 rows at N = K = 8192): there the skinny kernel stops at 32 rows.
+constexpr int64_t kSkSliceMaxM = 48;
+constexpr int64_t kSkSliceMaxMSplit = 32;
+
+// Whether a dense 16-bit call with M rows takes the skinny kernel: up to
+// kSkSliceMaxMSplit rows always, up to kSkSliceMaxM unless the NT kernel
+// would split K with the workspace given.
+template <int E>
+bool skinny_takes(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int b_layout, const void* ws,
+                  int64_t ws_bytes)
+{
+    if (M > kSkSliceMaxM || b_layout != TG_COL_MAJOR || K <= 0 ||
+        !skinny_offsets_fit(K, lda, ldb, SkinnyCfg::RING, skinny_cg(M)))
+        return false;
+    if (M <= kSkSliceMaxMSplit || ws == nullptr)
+        return true;
+    TileArgs t{};
+    t.M = M;
+    t.N = N;
+    t.K = K;
+    t.lda = lda;
+    t.ldb = ldb;
+    if (!nt_eligible<E>(t))
+        return true;
+    const NtPlan plan = plan_nt<E, B_KCONTIG>(M, N, K, true);
+    return !(plan.splits > 1 && plan.ws_bytes <= ws_bytes);
+}
 
 // fp16 / bf16 GEMM.  Few rows (kSkSliceMaxM) against a K-contiguous B take
 // the skinny kernel; everything else the tile kernel (K == 0 runs it with no
@@ -378,14 +420,14 @@ tg_status gemm_16bit(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
         return st;
     hipStream_t s = (hipStream_t)stream;
     typedef SkinnyCfg G;
-    if (M <= kSkSliceMaxM && b_layout == TG_COL_MAJOR && K > 0 && skinny_offsets_fit(K, lda, ldb, G::RING)) {
+    if (skinny_takes<E>(M, N, K, lda, ldb, b_layout, ws, ws_bytes)) {
         SkinnyArgs sa{M, N, K, (const uint8_t*)A, lda, (const uint8_t*)B, ldb, C, ldc};
         const int64_t blocks = skinny_blocks(M, N);
         if (blocks > 0x7FFFFFFF)
             return TG_ERR_NOT_SUPPORTED;
         const int split = skinny_split(blocks, K);
         if (split > 1) {  // narrow N: split K over workgroups too
-            const int64_t need = skinny_ws_bytes(blocks, split);
+            const int64_t need = skinny_ws_bytes(M, blocks, split);
             if (ws != nullptr && need > 0 && need <= ws_bytes) {
                 // partial tiles in the workspace, the last arrival stores C: any output type
                 sa.counters = (uint32_t*)ws;
@@ -465,9 +507,9 @@ int64_t dense_ws_bytes(int64_t M, int64_t N, int64_t K, int b_layout)
     constexpr int CE = 16 / ElemInfo<E>::bytes;
     if (M <= 0 || N <= 0 || K <= 0 || !dims_fit(M, N, K))
         return 0;
-    if (E != E_FP8 && M <= kSkSliceMaxM && b_layout == TG_COL_MAJOR) {  // the skinny kernel (any K)
+    if (E != E_FP8 && M <= kSkSliceMaxMSplit && b_layout == TG_COL_MAJOR) {  // the skinny kernel (any K)
         const int64_t blocks = skinny_blocks(M, N);
-        return skinny_ws_bytes(blocks, skinny_split(blocks, K));
+        return skinny_ws_bytes(M, blocks, skinny_split(blocks, K));
     }
     if (K % CE != 0)
         return 0;
