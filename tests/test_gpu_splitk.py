@@ -187,6 +187,31 @@ def test_skinny_split_workspace(tg, dt, out, shape):
     assert torch.equal(C.view(torch.int16) if out != "f32" else C, C2.view(torch.int16) if out != "f32" else C2)
 
 
+# 33 .. 48 rows against a K-contiguous B: the skinny kernel in row slices,
+# unless a caller workspace lets the NT kernel split K.  Where the NT plan
+# does not split (too few K steps) tg_gemm_ex with a workspace takes the same
+# kernel as the plain entry point, bit for bit; where it splits, the NT
+# kernel's result meets the bound.
+@pytest.mark.parametrize("shape,nt_splits", [((40, 1000, 256), False), ((48, 264, 448), False),
+                                             ((33, 2056, 4096), True), ((48, 1000, 8192), True)],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_skinny_or_split_nt_above_32_rows(tg, shape, nt_splits):
+    M, N, K = shape
+    need = tg.tg_gemm_ex_workspace_bytes(torch.bfloat16, M, N, K)
+    assert (need > 0) == nt_splits
+    A, B, _, _ = _inputs("bf16", M, N, K, "col", seed=M + N + K + 11)
+    Cx = _run(tg, A, B, "col", "bf16", 1.0, 1.0, _workspace(max(need, 4096)))
+    Cp = torch.full_like(Cx, float("nan"))
+    tg.tg_gemm_bf16(_dev(A), _dev(B), Cp, b_layout="col")
+    torch.cuda.synchronize()
+    if not nt_splits:
+        assert torch.equal(Cx.view(torch.int16), Cp.view(torch.int16)), "same kernel, different bits"
+    cref, S = oracle.gemm(oracle.BF16, A, B, oracle.B_NK)
+    for C in (Cx, Cp):
+        ok, r, idx = ochk.check(C.float().cpu().double().numpy(), cref, S, K, "bf16")
+        assert ok, (r, idx)
+
+
 # ---------------------------------------------------------------- w4a16
 # tg_gemm_w4a16_ex: the 128 x 128 w4a16 kernel with K split over workgroups
 # (each dequantised word feeds four MFMAs).  The w4a16 workload itself, and
