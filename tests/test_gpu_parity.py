@@ -697,6 +697,30 @@ def test_exact_one_hot_256_tile(tg, dt):
     assert torch.equal(C.cpu(), ref)
 
 
+# One-hot rows of A through the skinny kernel: each output sums one nonzero
+# product over the waves' K ranges, the LDS reduction of their partial
+# tiles and (narrow N, fp32 output) the atomic adds of the workgroups'
+# partial tiles, so C[i][n] = B[n][k_i] exactly.  16-column workgroups (one
+# slice: 8 and 16 rows), 32-column ones (row slices up to 48 rows), K tails
+# (K % 64) and the K split over workgroups.
+SKINNY_ONE_HOT = [(16, 8192, 4096), (8, 200, 1000), (40, 1000, 2072), (48, 264, 1024), (16, 1024, 8192),
+                  (24, 100, 4101)]
+
+
+@pytest.mark.parametrize("shape", SKINNY_ONE_HOT, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_skinny_one_hot_exact(tg, dt, shape):
+    M, N, K = shape
+    Bs = synth.normal((N, K), 910 + M, std=0.05).to(TDT[dt])
+    ks = torch.randint(0, K, (M,), generator=torch.Generator().manual_seed(911 + K))
+    ks[: min(M, 8)] = torch.tensor([0, K - 1, 63, 64, K // 2, K // 2 + 1, 31, 32])[: min(M, 8)]
+    A = torch.zeros((M, K))
+    A[torch.arange(M), ks] = 1.0
+    C = _run_dense(tg, dt, A.to(TDT[dt]), Bs, "col", "f32")
+    ref = Bs.float().t()[ks]
+    assert torch.equal(C.cpu(), ref)
+
+
 def test_workload_bf16_skinny(tg):
     w = synth.workload("bf16_skinny")
     C = _run_dense(tg, "bf16", w["A"], w["B"], "col", "f32")
