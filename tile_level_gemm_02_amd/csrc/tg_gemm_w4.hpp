@@ -486,13 +486,29 @@ template <int AI, int NT> struct W4dLayout {
     static constexpr int SLOT = QB + AB + SB;
 };
 
-template <int AI, int WAVES, int RING, int NT = 2>
+// Largest K range per wave with PRE (one A row and the scales held for the
+// whole range): K <= kW4PreMaxKW * waves.
+constexpr int kW4PreMaxKW = 4096;
+
+// PRE (one row, AI = 1, 16 columns): each wave copies its K range of the A
+// row (K_w * 2 bytes, 1 KiB per instruction) and its columns' scales for
+// that range (4 stages of 16 columns per 256-byte instruction) into LDS
+// once, before the ring, which then carries only the int4 words.  Per
+// stage the ring otherwise copies two A rows of 256 k and 256 bytes of
+// scales for 64 bytes used: at N = K = 8192 a timing-only copy without
+// those copies ran 11.5 against 13.3 us per flushed launch.
+template <int AI, int WAVES, int RING, int NT = 2, bool PRE = false>
 __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
 {
     typedef W4dLayout<AI, NT> L;
-    constexpr int SLOT = L::SLOT, QB = L::QB, AB = L::AB, COLS = L::COLS;
-    constexpr int PER = 2 * NT + AI + 1;  // copy instructions per stage: words, A rows, scales
-    constexpr int ZERO = WAVES * RING * SLOT;  // 16 zero bytes shared by every wave
+    constexpr int QB = L::QB, AB = L::AB, COLS = L::COLS;
+    static_assert(!PRE || (AI == 1 && NT == 1), "PRE: one A row, 16 columns");
+    constexpr int SLOT = PRE ? QB : L::SLOT;           // ring slot: words (and A rows and scales)
+    constexpr int APRE = PRE ? kW4PreMaxKW * 2 : 0;    // PRE: the wave's A row
+    constexpr int SPRE = PRE ? kW4PreMaxKW / 256 * COLS * 4 : 0;  // PRE: [stage][column] scale pairs
+    constexpr int WBYTES = RING * SLOT + APRE + SPRE;  // per wave
+    constexpr int PER = PRE ? 2 * NT : 2 * NT + AI + 1;  // copy instructions per stage: words (A rows, scales)
+    constexpr int ZERO = WAVES * WBYTES;  // 16 zero bytes shared by every wave
     static_assert(ZERO + 16 <= 160 * 1024 && WAVES * NT * 4 * 64 * 4 <= ZERO, "LDS");
     static_assert(AI >= 1 && AI <= 8 && RING >= 2 && (RING - 1) * PER <= 63, "copy ring");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[ZERO + 16];
@@ -513,7 +529,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
     const int64_t M = p.M - 16 * slice < 16 ? p.M - 16 * slice : 16;  // rows of this slice
     const int64_t KG = K / 128;  // a multiple of 2*WAVES: every wave gets whole stages
     const int64_t g0 = KG * wave / WAVES, nst = KG / (2 * WAVES);
-    uint8_t* ring = lds + wave * (RING * SLOT);
+    uint8_t* ring = lds + wave * WBYTES;
+    uint8_t* const apre = ring + RING * SLOT;  // PRE: stage st's 256 k of the A row at apre + 512 st
+    uint8_t* const spre = apre + APRE;         // PRE: column c's scale pair of stage st at spre + 4 (COLS st + c)
     if (tid == 0)
         *(u32x4*)(lds + ZERO) = u32x4{0u, 0u, 0u, 0u};
 
@@ -547,10 +565,31 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
 #pragma unroll
         for (int i = 0; i < 2 * NT; ++i)
             load_lds_1k(rq, slot + i * 1024, vq[i] | past, g * 64u);
+        if constexpr (!PRE) {
 #pragma unroll
-        for (int i = 0; i < AI; ++i)
-            load_lds_1k(ra, slot + QB + i * 1024, va[i] | past, g * 256u);
-        load_lds_256(rs, slot + QB + AB, vs | past, g * 2u);
+            for (int i = 0; i < AI; ++i)
+                load_lds_1k(ra, slot + QB + i * 1024, va[i] | past, g * 256u);
+            load_lds_256(rs, slot + QB + AB, vs | past, g * 2u);
+        }
+    };
+    // PRE: the wave's A row (instruction i: k = 128 g0 + 512 i + 8 lane ..
+    // +7) and scale pairs (instruction i: stage 4i + lane/16 of column
+    // lane%16), lanes past the wave's range or past N reading zeros; issued
+    // before the ring, so every wait for a stage also covers them
+    auto preload = [&]() __attribute__((always_inline)) {
+        const int64_t kend = (g0 + 2 * nst) * 128;  // end of the wave's K range
+        for (int64_t i = 0; i < (nst + 1) / 2; ++i) {
+            const int64_t k = g0 * 128 + 512 * i + 8 * (int64_t)lane;
+            load_lds_1k(ra, apre + i * 1024, k < kend ? lane * 16u : kOutOfRange,
+                        (uint32_t)(g0 * 256 + 1024 * i));
+        }
+        const uint32_t c = lane % 16u;
+        for (int64_t i = 0; i < (nst + 3) / 4; ++i) {
+            const int64_t st = 4 * i + lane / 16u;
+            const bool ok = st < nst && n0 + c < N;
+            load_lds_256(rs, spre + i * 256, ok ? c * (uint32_t)p.lds * 2u + (lane / 16u) * 4u : kOutOfRange,
+                         (uint32_t)(g0 * 2 + 16 * i));
+        }
     };
 
     const W4Consts wc = w4_consts(p.zero_point);
@@ -559,12 +598,12 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
     for (int t = 0; t < NT; ++t)
         acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint32_t c = lane & 15u, h = lane >> 4;  // MFMA lane: column (or row) c, quarter h
-    const bool arow = c < 2u * AI;                  // this lane's A row is held in the slot
+    const bool arow = c < (PRE ? 1u : 2u * AI);     // this lane's A row is held in LDS (else zeros)
 
     // One stage: every LDS read first (words, scales and A chunks of both
     // groups), so a wave pays the LDS latency once per stage instead of once
     // per MFMA; then the dequant and the MFMAs, in the same order as before.
-    auto compute = [&](const uint8_t* slot) __attribute__((always_inline)) {
+    auto compute = [&](const uint8_t* slot, int64_t st) __attribute__((always_inline)) {
         u32x4 q[2][NT], a[2][4];
         _Float16 sc[2][NT];
 #pragma unroll
@@ -574,14 +613,18 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
                 const uint32_t col = 16u * t + c;
                 const uint32_t phys = (4u * u + h) ^ ((col >> 1) & 7u);
                 q[u][t] = lds128(slot, col * 128u + phys * 16u);
-                sc[u][t] = bit_cast<_Float16>(*(const uint16_t*)(slot + QB + AB + col * 4u + u * 2u));
+                const uint8_t* sp = PRE ? spre + ((uint32_t)st * COLS + col) * 4u : slot + QB + AB + col * 4u;
+                sc[u][t] = bit_cast<_Float16>(*(const uint16_t*)(sp + u * 2u));
             }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t phys = (16u * u + 4u * h + j) ^ c;
-                a[u][j] = lds128(lds, arow ? (uint32_t)(slot - lds) + QB + c * 512u + phys * 16u : (uint32_t)ZERO);
+                // (PRE: row 0 only, unswizzled: c = 0 where it is read)
+                const uint32_t arow_at = PRE ? (uint32_t)(apre - lds) + (uint32_t)st * 512u + phys * 16u
+                                             : (uint32_t)(slot - lds) + QB + c * 512u + phys * 16u;
+                a[u][j] = lds128(lds, arow ? arow_at : (uint32_t)ZERO);
             }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -595,6 +638,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
 
     __syncthreads();  // the zero block is written
     if (nst > 0) {
+        if constexpr (PRE)
+            preload();
 #pragma unroll
         for (int r = 0; r < RING - 1; ++r)
             issue(r, ring + r * SLOT);
@@ -602,9 +647,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_w4_lds(TileArgs p)
         for (int64_t st = 0; st < nst; ++st) {
             const uint32_t nxt = cur >= 1 ? cur - 1 : RING - 1;  // slot of stage st+RING-1 == slot of st-1
             issue(st + RING - 1, ring + nxt * SLOT);
-            wait_copies<(RING - 1) * PER>();  // this wave's copies of stage st have landed
+            wait_copies<(RING - 1) * PER>();  // this wave's copies of stage st (and all before them) have landed
             __builtin_amdgcn_sched_barrier(0);
-            compute(ring + cur * SLOT);
+            compute(ring + cur * SLOT, st);
             __builtin_amdgcn_sched_barrier(0);
             cur = cur + 1 == RING ? 0 : cur + 1;
         }

@@ -100,7 +100,9 @@ bool w4_skinny_lds_eligible(const tg::TileArgs& a, int waves, int cols, int ring
 }
 
 // launches the LDS decode kernel for AI A-copy instructions per stage, or
-// returns false (nothing launched) if the problem does not fit its shape
+// returns false (nothing launched) if the problem does not fit its shape.
+// One row with each wave's K range at most kW4PreMaxKW takes the variant
+// that copies A and the scales once per wave (PRE).
 template <int AI>
 bool launch_skinny_lds(const tg::TileArgs& a, hipStream_t s, tg_status* st)
 {
@@ -108,6 +110,7 @@ bool launch_skinny_lds(const tg::TileArgs& a, hipStream_t s, tg_status* st)
     constexpr int COLS = tg::W4dLayout<AI, G::NT>::COLS;
     if (!w4_skinny_lds_eligible(a, G::WAVES, COLS, G::RING))
         return false;
+
     // one workgroup per column block and 16-row slice of M; with several
     // slices the column blocks are padded to a multiple of 8 (see the kernel)
     const int64_t nblk = (a.N + COLS - 1) / COLS, slices = (a.M + 15) / 16;
@@ -115,6 +118,14 @@ bool launch_skinny_lds(const tg::TileArgs& a, hipStream_t s, tg_status* st)
     if (blocks > 0x7FFFFFFF) {
         *st = TG_ERR_NOT_SUPPORTED;
         return true;
+    }
+    if constexpr (AI == 1 && G::NT == 1) {
+        if (a.M == 1 && a.K / G::WAVES <= tg::kW4PreMaxKW) {
+            hipLaunchKernelGGL((tg::skinny_w4_lds<AI, G::WAVES, G::RING, G::NT, true>), dim3((uint32_t)blocks),
+                               dim3(G::WAVES * 64), 0, s, a);
+            *st = tg::launched();
+            return true;
+        }
     }
     hipLaunchKernelGGL((tg::skinny_w4_lds<AI, G::WAVES, G::RING, G::NT>), dim3((uint32_t)blocks), dim3(G::WAVES * 64), 0,
                        s, a);
