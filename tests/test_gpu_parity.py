@@ -485,7 +485,8 @@ def test_w4a16_layouts(tg, case):
 # M <= 16: the decode kernels.  K a multiple of 1024 (four waves) takes the
 # LDS-ring kernel (one instantiation per A copy count: M <= 2, 4, 8, 16; 16
 # columns per workgroup for M <= 4, 32 above; a single stage per wave and
-# several);
+# several; one row with K up to 16384 copies A and the scales once per wave,
+# above it per stage);
 # other K the register kernel (eight waves split the 128-K groups: a group
 # count below, equal to and not a multiple of the wave count, here also at
 # 1280, 2304 and 256).  Ragged N, both ends of the zero-point range.
@@ -493,7 +494,8 @@ def test_w4a16_layouts(tg, case):
                                    (16, 520, 2176), (5, 64, 1024), (1, 1000, 4096),
                                    (2, 72, 2048), (3, 33, 3072), (8, 100, 1024), (9, 64, 2048),
                                    (16, 520, 1024), (16, 40, 8192), (4, 31, 5120), (3, 33, 6144),
-                                   (4, 100, 2048), (1, 300, 1280), (16, 72, 2304), (6, 8, 256)],
+                                   (4, 100, 2048), (1, 300, 1280), (16, 72, 2304), (6, 8, 256),
+                                   (1, 136, 16384), (1, 72, 17408), (1, 40, 3072)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("zp", [0, 15])
 def test_w4a16_decode(tg, shape, zp):
