@@ -300,8 +300,8 @@ def main():
                     help="only run this workload's launches (for counter collection), no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the GEMM would shard by output columns with no exchange; see the design notes)",
+        print(f"bench.py: the library and this benchmark run on one GPU; --gpus {args.gpus} is not supported "
+              "(over several GPUs the GEMM would shard by output columns, with no exchange between them)",
               file=sys.stderr)
         sys.exit(2)
 
