@@ -52,17 +52,17 @@ def _pair(tg, dt, out, M, N, K, seed):
 
 # in a row, each smaller than the one before: the largest split plan
 # (16 MiB of partial tiles), a smaller one on the 64 tile, an fp8 one, the
-# skinny kernel's split with a 16-bit output, and a problem that does not
-# split
+# skinny kernel's split with a 16-bit output (16 columns per workgroup, then
+# 32 in two row slices), and a problem that does not split
 CALLS = [("bf16", "bf16", 256, 8192, 8192), ("bf16", "bf16", 64, 1024, 8192), ("fp8", "f32", 40, 1000, 4096),
-         ("bf16", "bf16", 16, 1024, 8192), ("f16", "f16", 9, 200, 1000)]
+         ("bf16", "bf16", 16, 1024, 8192), ("f16", "f16", 24, 520, 2048), ("f16", "f16", 9, 200, 1000)]
 
 
 def test_noalloc_matches_gemm_ex_in_a_row(tg):
     for i, (dt, out, M, N, K) in enumerate(CALLS):
         print(f"noalloc call {i}: {dt} {M}x{N}x{K} -> {out}", flush=True)
         C1, C2, (A, B, sa, sb), need = _pair(tg, dt, out, M, N, K, seed=100 + i)
-        if i < 4:
+        if i < len(CALLS) - 1:
             assert need > 0, "expected a split plan"
         eq = torch.equal(C1.view(torch.int16), C2.view(torch.int16)) if out != "f32" else torch.equal(C1, C2)
         assert eq, f"call {i}: noalloc output differs from tg_gemm_ex"
