@@ -136,8 +136,11 @@ def setup_skinny():
     return w, fn, flops, bytes_
 
 
-def setup_skinny_shard():
-    """The skinny workload's 8-way column shard: M=16, N=1024, K=8192."""
+def setup_skinny_shard(ws_split: bool = False):
+    """The skinny workload's 8-way column shard: M=16, N=1024, K=8192.  The
+    plain entry point splits K by atomic adds into a C that a fill kernel
+    zeroes first; with a workspace (tg_gemm_ex) the split hands its partial
+    tiles to the last arrival and no fill runs."""
     import torch
     import synth
     import tile_level_gemm_02_amd as tg
@@ -145,7 +148,12 @@ def setup_skinny_shard():
     w = synth.workload("bf16_skinny", N=1024)
     A, B = w["A"].cuda(), w["B"].cuda()
     C = torch.empty((w["M"], w["N"]), dtype=torch.float32, device="cuda")
-    fn = lambda: tg.tg_gemm_bf16(A, B, C, b_layout="col")
+    if ws_split:
+        need = tg.tg_gemm_ex_workspace_bytes(torch.bfloat16, w["M"], w["N"], w["K"])
+        ws = torch.zeros(max(need, 256) // 4, dtype=torch.int32, device="cuda")
+        fn = lambda: tg.tg_gemm_ex(A, B, C, b_layout="col", workspace=ws)
+    else:
+        fn = lambda: tg.tg_gemm_bf16(A, B, C, b_layout="col")
     flops = 2.0 * w["M"] * w["N"] * w["K"]
     bytes_ = 2 * (w["M"] * w["K"] + w["N"] * w["K"]) + 4 * w["M"] * w["N"]
     return w, fn, flops, bytes_
@@ -293,7 +301,7 @@ def main():
                     help="with --only: no cache flush between the launches (sustained load, e.g. to sample clocks)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (to scale HBM byte counters)")
-    ap.add_argument("--only", choices=["bf16_4096", "bf16_skinny", "bf16_skinny_n1024", "fp8_8192", "fp8_8192_rowb",
+    ap.add_argument("--only", choices=["bf16_4096", "bf16_skinny", "bf16_skinny_n1024", "bf16_skinny_n1024_ws", "fp8_8192", "fp8_8192_rowb",
                                        "w4a16", "w4a16_split", "w4a16_m16", "w4a16_m1", "sp24_4096", "bf16_m256",
                                        "bf16_m256_split"],
                     default=None,
@@ -324,7 +332,7 @@ def main():
     flush = make_flush()
     if args.only:
         setup = {"bf16_4096": setup_bf16_4096, "bf16_skinny": setup_skinny, "bf16_skinny_n1024": setup_skinny_shard,
-                 "fp8_8192": setup_fp8, "fp8_8192_rowb": setup_fp8_rowb,
+                 "bf16_skinny_n1024_ws": lambda: setup_skinny_shard(True), "fp8_8192": setup_fp8, "fp8_8192_rowb": setup_fp8_rowb,
                  "bf16_m256": lambda: setup_bf16_m256(False), "bf16_m256_split": lambda: setup_bf16_m256(True),
                  "w4a16": setup_w4a16, "w4a16_split": lambda: setup_w4a16(split=True), "w4a16_m16": lambda: setup_w4a16(16), "sp24_4096": setup_sp24,
                  "w4a16_m1": lambda: setup_w4a16(1)}[args.only]
@@ -393,6 +401,7 @@ def main():
         sec = {}
         n = max(10, min(args.steps, 50))
         for name, setup, peak_key in (("bf16_skinny", setup_skinny, "hbm"), ("bf16_skinny_n1024", setup_skinny_shard, "hbm"),
+                                      ("bf16_skinny_n1024_ws", lambda: setup_skinny_shard(True), "hbm"),
                                       ("fp8_8192", setup_fp8, "fp8"),
                                       ("w4a16", setup_w4a16, "both"),
                                       ("w4a16_split", lambda: setup_w4a16(split=True), "both"),

@@ -252,12 +252,13 @@ def test_row_major_b_large(tg):
     assert torch.equal(C, C2), "repeated runs differ"
 
 
-# Narrow N with fp32 output (a column shard of the skinny workload): the
+# Narrow N with fp32 output (a column shard of the skinny workload): where
+# K gives each of four or more workgroups per column block 2048 of it, the
 # skinny kernel also splits K over workgroups and adds their partial tiles
 # into a zeroed C with fp32 atomics.  Ragged N and K, a split count that does
 # not divide the K blocks, a K tail inside the last split, and K too short
 # to split.
-@pytest.mark.parametrize("shape", [(16, 1024, 8192), (5, 512, 4104), (1, 64, 2048), (16, 1000, 1000),
+@pytest.mark.parametrize("shape", [(16, 1024, 8192), (5, 512, 8200), (1, 64, 2048), (16, 1000, 1000),
                                    (3, 40, 8200), (16, 33, 30000)], ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_skinny_split_k(tg, dt, shape):
@@ -270,7 +271,7 @@ def test_skinny_split_k(tg, dt, shape):
 def test_skinny_split_k_leaves_padding(tg):
     """The split path zeroes and adds into C's M x N entries only; columns past N
     in a padded row are left alone, and a second call gives the same result."""
-    M, N, K = 9, 200, 6144
+    M, N, K = 9, 200, 8256
     A, B, _, _ = _inputs("bf16", M, N, K, "col", seed=91)
     store = torch.full((M, N + 24), 5.0, dtype=torch.float32, device="cuda")
     C = store[:, :N]
@@ -706,7 +707,7 @@ def test_exact_one_hot_256_tile(tg, dt):
 # slice: 8 and 16 rows), 32-column ones (row slices up to 48 rows), K tails
 # (K % 64) and the K split over workgroups.
 SKINNY_ONE_HOT = [(16, 8192, 4096), (8, 200, 1000), (40, 1000, 2072), (48, 264, 1024), (16, 1024, 8192),
-                  (24, 100, 4101)]
+                  (24, 100, 8197)]
 
 
 @pytest.mark.parametrize("shape", SKINNY_ONE_HOT, ids=lambda s: "x".join(map(str, s)))

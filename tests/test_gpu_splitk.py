@@ -167,7 +167,7 @@ def test_workspace_errors(tg):
 # splits only fp32 outputs, by atomic adds into a zeroed C).  Ragged N, K
 # tails (K % 64, and a partial 16-byte chunk), a split count that does not
 # divide the K stages, and row slices.
-SKINNY_SPLIT = [(16, 1024, 8192), (5, 520, 4104), (1, 64, 2048), (3, 40, 8200), (24, 200, 6144), (32, 264, 4101)]
+SKINNY_SPLIT = [(16, 1024, 8192), (5, 520, 4104), (1, 64, 4160), (3, 40, 8200), (24, 200, 6144), (32, 264, 4101)]
 
 
 @pytest.mark.parametrize("shape", SKINNY_SPLIT, ids=lambda s: "x".join(map(str, s)))

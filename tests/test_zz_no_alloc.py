@@ -55,7 +55,7 @@ def _pair(tg, dt, out, M, N, K, seed):
 # skinny kernel's split with a 16-bit output (16 columns per workgroup, then
 # 32 in two row slices), and a problem that does not split
 CALLS = [("bf16", "bf16", 256, 8192, 8192), ("bf16", "bf16", 64, 1024, 8192), ("fp8", "f32", 40, 1000, 4096),
-         ("bf16", "bf16", 16, 1024, 8192), ("f16", "f16", 24, 520, 2048), ("f16", "f16", 9, 200, 1000)]
+         ("bf16", "bf16", 16, 1024, 8192), ("f16", "f16", 24, 520, 4096), ("f16", "f16", 9, 200, 1000)]
 
 
 def test_noalloc_matches_gemm_ex_in_a_row(tg):

@@ -309,15 +309,23 @@ struct SkinnyCfg {
     static constexpr int WAVES = 8, RING = 2;
 };
 
-// Workgroups per column block of the skinny kernel: two workgroups per CU
-// (512) when N alone gives fewer, keeping at least two 64-wide K stages per
-// wave.
-inline int skinny_split(int64_t blocks, int64_t K)
+// Workgroups per column block of the skinny kernel when N alone gives few:
+// about one per CU (256 in all), each with at least 2048 of K.  Without a
+// workspace (fp32 atomic adds into a C that a fill launch zeroes first) only
+// a split into four or more pays for the fill.  Flushed launches, M = 16,
+// K = 8192, 16-bit inputs: with a workspace N = 512 14.4 -> 10.7 us (4
+// splits) and N = 2048 15.4 -> 13.5 us (2), where two workgroups per CU (8
+// splits at N = 512, 4 at N = 2048) took 12.1 and 16.3 us; by atomics
+// N = 1024 14.5 -> 13.0 us (4), while 2 or 3 splits ran 0.4-2.4 us slower
+// than none at every N and K measured.
+inline int skinny_split(int64_t blocks, int64_t K, bool atomic)
 {
-    int64_t split = (512 + blocks - 1) / blocks;
-    const int64_t most = K / kSkKE / (SkinnyCfg::WAVES * 2);
+    int64_t split = 256 / blocks;
+    const int64_t most = K / 2048;
     if (split > most)
         split = most;
+    if (atomic && split < 4)
+        split = 1;
     return split > 1 ? (int)split : 1;
 }
 
@@ -425,26 +433,26 @@ tg_status gemm_16bit(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
         const int64_t blocks = skinny_blocks(M, N);
         if (blocks > 0x7FFFFFFF)
             return TG_ERR_NOT_SUPPORTED;
-        const int split = skinny_split(blocks, K);
-        if (split > 1) {  // narrow N: split K over workgroups too
-            const int64_t need = skinny_ws_bytes(M, blocks, split);
-            if (ws != nullptr && need > 0 && need <= ws_bytes) {
-                // partial tiles in the workspace, the last arrival stores C: any output type
-                sa.counters = (uint32_t*)ws;
-                sa.partials = (float*)((uint8_t*)ws + kSplitCounterBytes);
-                switch (c_dtype) {
-                case TG_F32: launch_skinny<E, O_F32, 2>(sa, blocks, split, s); break;
-                case TG_F16: launch_skinny<E, O_F16, 2>(sa, blocks, split, s); break;
-                default: launch_skinny<E, O_BF16, 2>(sa, blocks, split, s); break;
-                }
-                return launched();
+        // narrow N: split K over workgroups too
+        const int split = skinny_split(blocks, K, false);
+        const int64_t need = split > 1 ? skinny_ws_bytes(M, blocks, split) : 0;
+        if (ws != nullptr && need > 0 && need <= ws_bytes) {
+            // partial tiles in the workspace, the last arrival stores C: any output type
+            sa.counters = (uint32_t*)ws;
+            sa.partials = (float*)((uint8_t*)ws + kSplitCounterBytes);
+            switch (c_dtype) {
+            case TG_F32: launch_skinny<E, O_F32, 2>(sa, blocks, split, s); break;
+            case TG_F16: launch_skinny<E, O_F16, 2>(sa, blocks, split, s); break;
+            default: launch_skinny<E, O_BF16, 2>(sa, blocks, split, s); break;
             }
-            if (c_dtype == TG_F32) {  // no workspace: fp32 atomic adds into a zeroed C
-                hipLaunchKernelGGL(zero_f32<>, dim3((uint32_t)((N + 1023) / 1024), (uint32_t)M), dim3(256), 0, s, (float*)C,
-                                   N, ldc);
-                launch_skinny<E, O_F32, 1>(sa, blocks, split, s);
-                return launched();
-            }
+            return launched();
+        }
+        const int asplit = c_dtype == TG_F32 ? skinny_split(blocks, K, true) : 1;
+        if (asplit > 1) {  // no workspace: fp32 atomic adds into a zeroed C
+            hipLaunchKernelGGL(zero_f32<>, dim3((uint32_t)((N + 1023) / 1024), (uint32_t)M), dim3(256), 0, s, (float*)C,
+                               N, ldc);
+            launch_skinny<E, O_F32, 1>(sa, blocks, asplit, s);
+            return launched();
         }
         switch (c_dtype) {
         case TG_F32: launch_skinny<E, O_F32>(sa, blocks, 1, s); break;
@@ -509,7 +517,7 @@ int64_t dense_ws_bytes(int64_t M, int64_t N, int64_t K, int b_layout)
         return 0;
     if (E != E_FP8 && M <= kSkSliceMaxMSplit && b_layout == TG_COL_MAJOR) {  // the skinny kernel (any K)
         const int64_t blocks = skinny_blocks(M, N);
-        return skinny_ws_bytes(M, blocks, skinny_split(blocks, K));
+        return skinny_ws_bytes(M, blocks, skinny_split(blocks, K, false));
     }
     if (K % CE != 0)
         return 0;
