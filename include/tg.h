@@ -203,7 +203,10 @@ int64_t tg_gemm_ex_workspace_bytes(tg_input in, int64_t M, int64_t N, int64_t K,
  * that lets the library split K over several workgroups per output tile
  * where too few output tiles would leave the chip's compute units idle or
  * re-read the operands too often (e.g. a few hundred rows against an
- * 8192 x 8192 weight).  This is the split of K whose partial results are
+ * 8192 x 8192 weight), or where the output tiles take more than one round
+ * of the chip and the last round is short (e.g. 4608 x 4608: 324 tiles of
+ * 256 x 256 on 256 compute units): the full rounds then run whole tiles and
+ * only the last round's tiles split.  This is the split of K whose partial results are
  * summed on chip in the TileScale README's GEMM example (section "Example
  * of GEMM"), taken across workgroups: each workgroup accumulates its K
  * range in fp32, stores the fp32 partial tile in the workspace, and the
@@ -235,7 +238,7 @@ tg_status tg_gemm_ex(tg_input in, int64_t M, int64_t N, int64_t K,
 /* tg_gemm_ex without a caller workspace, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, and
  * harnesses that forbid allocation.  It allocates nothing: its split
- * workspace is a static device array of this library, 16 MiB + 64 KiB
+ * workspace is a static device array of this library, 64 MiB + 64 KiB
  * (every split plan the library makes fits in it), which each GPU holds from
  * the library's load until the process ends.  The first call with a device
  * current looks up that device's array and clears its 64 KiB of arrival

@@ -127,6 +127,64 @@ def test_split_one_hot_exact(tg, dt):
     assert torch.equal(C.cpu(), Bs.float().t()[ks])
 
 
+# More than one round of 256 x 256 tiles with a short last round: the plan
+# runs the full round's tiles whole and splits K only for the last round's
+# tiles (its workspace covers those alone), in one launch.  Ragged M, N and
+# K (a partial last K step), both layouts of B, 16-bit and fp8 inputs.
+def _last_round(M, N):
+    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+    return tiles, tiles - tiles // 256 * 256
+
+
+def _expect_last_round_split(tg, dt, M, N, K, lay):
+    tiles, R = _last_round(M, N)
+    assert tiles > 256 and 0 < R <= 128
+    need = tg.tg_gemm_ex_workspace_bytes(TDT[dt], M, N, K, lay)
+    per_split_tile = 256 * 256 * 4
+    assert need > 0 and (need - 65536) % (R * per_split_tile) == 0, "expected the last round's tiles split"
+    splits = (need - 65536) // (R * per_split_tile)
+    assert 2 <= splits and R * splits <= 256
+    print(f"{dt} {M}x{N}x{K} {lay}: {tiles} tiles, last round {R} tiles split {splits} ways", flush=True)
+    return need
+
+
+def test_last_round_split_parity(tg):
+    """Every element against the oracle's bound, a bit-identical repeat, and
+    the counters left zero."""
+    M, N, K = 4300, 4100, 8200
+    need = _expect_last_round_split(tg, "bf16", M, N, K, "col")
+    A, B, _, _ = _inputs("bf16", M, N, K, "col", seed=41)
+    ws = _shared_workspace(need)
+    C = _run(tg, A, B, "col", "bf16", 1.0, 1.0, ws)
+    assert int(ws[:COUNTER_WORDS].count_nonzero()) == 0
+    C2 = _run(tg, A, B, "col", "bf16", 1.0, 1.0, ws)
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16)), "repeated calls differ"
+    cref, S = oracle.gemm(oracle.BF16, A, B, oracle.B_NK)
+    ok, r, idx = ochk.check(C.float().cpu().double().numpy(), cref, S, K, "bf16")
+    assert ok, (r, idx)
+
+
+@pytest.mark.parametrize("dt,lay,shape", [("bf16", "col", (4300, 4100, 8200)), ("f16", "row", (4352, 4104, 8192)),
+                                          ("fp8", "col", (4300, 4104, 16384))],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_last_round_split_one_hot_exact(tg, dt, lay, shape):
+    """One-hot rows of A: each output of every tile, whole or split, sums one
+    nonzero product and zeros, so C equals B's entries exactly; a tile or a
+    K range mapped wrongly shows up as a wrong or missing entry."""
+    M, N, K = shape
+    need = _expect_last_round_split(tg, dt, M, N, K, lay)
+    Bs = _inputs(dt, 1, N, K, lay, seed=43)[1]
+    ks = torch.randint(0, K, (M,), generator=torch.Generator().manual_seed(44))
+    ks[:4] = torch.tensor([0, K - 1, K // 2, K // 2 - 1])
+    A = torch.zeros((M, K))
+    A[torch.arange(M), ks] = 1.0
+    ws = _shared_workspace(need)
+    C = _run(tg, A.to(TDT[dt]), Bs, lay, "f32", 1.0, 1.0, ws)
+    assert int(ws[:COUNTER_WORDS].count_nonzero()) == 0
+    ref = Bs.float().t()[ks] if lay == "col" else Bs.float()[ks]
+    assert torch.equal(C.cpu(), ref)
+
+
 def test_workspace_free_call_agrees(tg):
     """With no workspace tg_gemm_ex is the plain entry point, bit for bit;
     with one it agrees within the bound."""

@@ -170,10 +170,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
     // K split over S workgroups per tile (S = 1: none); this workgroup runs
     // K steps [kt0, kt0 + NK).  The ring below counts steps from kt0; global
-    // offsets use the absolute step kt0 + kt.
-    const uint32_t S = p.splits > 1u ? p.splits : 1u;
-    uint32_t tmi, tni, ks;
-    tile_split_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, S, p.group_m, tmi, tni, ks);
+    // offsets use the absolute step kt0 + kt.  With p.dp > 0 the first p.dp
+    // workgroups take the first p.dp tiles of the walk whole (one round of
+    // the chip) and the workgroups after them split the remaining tiles, so
+    // that a last round of few tiles still fills the compute units; split
+    // tiles are numbered from p.dp (`stile`) for their counters and shares.
+    uint32_t S = p.splits > 1u ? p.splits : 1u;
+    uint32_t tmi, tni, ks = 0u, stile;
+    if (p.dp == 0u) {
+        tile_split_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, S, p.group_m, tmi, tni, ks);
+        stile = tmi * tiles_n + tni;
+    } else if (blockIdx.x < p.dp) {
+        tile_coords(blockIdx.x, p.dp, tiles_m, tiles_n, p.group_m, tmi, tni);
+        S = 1u;
+        stile = 0u;
+    } else {
+        const uint32_t R = tiles_m * tiles_n - p.dp;  // tiles split, S workgroups each
+        const uint32_t idx = xcd_remap(blockIdx.x - p.dp, gridDim.x - p.dp);
+        ks = idx / R;
+        stile = idx - ks * R;
+        group_walk(p.dp + stile, tiles_m, tiles_n, p.group_m, tmi, tni);
+    }
     const int64_t m0 = (int64_t)tmi * BM, n0 = (int64_t)tni * BN;
     const uint32_t ldab = (uint32_t)(p.lda * EB), ldbb = (uint32_t)(p.ldb * EB);
     const int32_t rows_a = (int32_t)(M - m0 < BM ? M - m0 : BM);
@@ -465,7 +482,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     // share in its own LDS region.)
     if (S > 1u) {
         constexpr int SHARE = TM * TN * 1024;  // floats of a wave's share
-        const uint32_t tile = tmi * tiles_n + tni;
+        const uint32_t tile = stile;
         float* const share0 = p.partials + ((size_t)tile * S * NW + wave) * SHARE;  // split 0's slot
         auto slot = [&](uint32_t q) __attribute__((always_inline)) { return share0 + (size_t)q * NW * SHARE; };
 #pragma unroll

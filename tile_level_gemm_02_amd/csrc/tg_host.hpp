@@ -160,6 +160,7 @@ inline int64_t split_ws_bytes(int64_t tiles, int splits, int64_t tile_elems)
 struct NtPlan {
     int tile, nh, splits;
     int64_t ws_bytes;  // workspace the plan needs (0 without a split)
+    int64_t dp;        // > 0: this many tiles run whole, the rest split `splits` ways
 };
 
 // Estimated cycles of one compute unit for an NT launch with tile edge T and
@@ -170,23 +171,44 @@ struct NtPlan {
 // S - 1 and its own (device-coherent accesses, about 16 bytes per clock per
 // CU as fitted to splits measured at N = K = 8192); workgroups run in rounds
 // of one per CU.
-inline double nt_cost(int64_t M, int64_t N, int64_t K, int EB, int T, int S)
+inline double nt_round_cost(int64_t K, int EB, int T, int S)
 {
-    const double tiles = (double)(((M + T - 1) / T) * ((N + T - 1) / T));
     const double kw = (double)K / S;  // K elements per workgroup
     const double copy = 2.0 * T * kw * EB / 37.0;
     const double mfma = 2.0 * T * T * kw / (EB == 1 ? 8192.0 : 4096.0);
     const double red = S > 1 ? (double)T * T * 4.0 * (S + 1) / 16.0 : 0.0;
     const double fixed = 4000.0;  // ring fill and epilogue
+    return (copy > mfma ? copy : mfma) + red + fixed;
+}
+
+// Cycles of one compute unit for a 256 x 256 tile running K / S of K in the
+// last round of a launch that splits only that round (S = 1: a whole tile):
+// the K loop at the rate measured for this tile, about 1.17 times its MFMA
+// issue time; the ring fill and epilogue; with S > 1 about 16 K cycles per
+// split for the hand-off of the 256 KiB partial tiles (fitted to last-round
+// splits timed back to back at 4608^3, 6144^3, 7168^3, 9216 x 9216 x 4096,
+// 4300 x 4104 x 8200 and 3000 x 6000 x 4096: the split count this picks ran
+// fastest, or within 1% of it, at each).
+inline double nt_round256_cost(int64_t K, int EB, int S)
+{
+    const double kw = (double)K / S;
+    const double copy = 2.0 * 256 * kw * EB / 37.0;
+    const double mfma = 2.0 * 256 * 256 * kw / (EB == 1 ? 8192.0 : 4096.0);
+    return 1.17 * (copy > mfma ? copy : mfma) + 4000.0 + (S > 1 ? 16384.0 * S : 0.0);
+}
+
+inline double nt_cost(int64_t M, int64_t N, int64_t K, int EB, int T, int S)
+{
+    const double tiles = (double)(((M + T - 1) / T) * ((N + T - 1) / T));
     const double rounds = (double)((int64_t)(tiles * S + 255.0) / 256);
-    return rounds * ((copy > mfma ? copy : mfma) + red + fixed);
+    return rounds * nt_round_cost(K, EB, T, S);
 }
 
 template <int E, int BL>
 NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
 {
     constexpr int EB = ElemInfo<E>::bytes;
-    NtPlan p{pick_tile(M, N, true), 4, 1, 0};
+    NtPlan p{pick_tile(M, N, true), 4, 1, 0, 0};
     if (EB == 1 && BL == B_NCONTIG && p.tile < 128)
         p.tile = 128;  // (nt_eligible_nrow only admits shapes that pick 128 or 256)
     if (allow_split) {
@@ -213,8 +235,33 @@ NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
                 }
             }
         }
+        // More than one round of 256 tiles with a short last round: the full
+        // rounds run whole tiles and the last round's R tiles split K S ways
+        // (R * S <= 256 workgroups, dispatched right behind the whole tiles).
+        if (p.tile == 256 && p.splits == 1) {
+            const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+            const int64_t D = tiles256 / 256 * 256, R = tiles256 - D;
+            if (D > 0 && R > 0 && R * 2 <= 256 && R * nt_waves(256) <= kSplitMaxCounters) {
+                const double whole = (double)(D / 256) * nt_round256_cost(K, EB, 1);
+                const double unsplit = whole + nt_round256_cost(K, EB, 1);
+                double hbest = unsplit;
+                int hs = 1;
+                for (int S = 2; R * S <= 256 && KT / S >= 8; ++S) {
+                    const double c = whole + nt_round256_cost(K, EB, S);
+                    if (c < hbest) {
+                        hbest = c;
+                        hs = S;
+                    }
+                }
+                if (hs > 1 && hbest < unsplit * 0.97) {  // (a clear gain over the whole-tile last round)
+                    p.splits = hs;
+                    p.dp = D;
+                }
+            }
+        }
     }
-    const int64_t tiles = ((M + p.tile - 1) / p.tile) * ((N + p.tile - 1) / p.tile);
+    const int64_t tiles = p.dp > 0 ? ((M + 255) / 256) * ((N + 255) / 256) - p.dp
+                                   : ((M + p.tile - 1) / p.tile) * ((N + p.tile - 1) / p.tile);
     // ring depth: the 256 tile per element type; the 128 and 64 tiles take 8
     // half-stages (4 steps in flight) when their workgroups fit the chip at
     // the occupancy that allows (one 128 KiB workgroup, or two of 64 KiB, per
@@ -228,14 +275,15 @@ NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
         p.nh = 8;
     else
         p.nh = tiles * p.splits <= 256 ? 8 : 4;
-    p.ws_bytes = split_ws_bytes(tiles, p.splits, (int64_t)p.tile * p.tile);
+    p.ws_bytes = split_ws_bytes(tiles, p.splits, (int64_t)p.tile * p.tile);  // (split tiles only)
     return p;
 }
 
 template <int E, int O, int BM, int BN, int BL, int NH>
 tg_status launch_nt(const TileArgs& a, int splits, hipStream_t s)
 {
-    const int64_t grid = n_tiles<BM, BN>(a.M, a.N) * splits;
+    const int64_t tiles = n_tiles<BM, BN>(a.M, a.N);
+    const int64_t grid = a.dp > 0 ? a.dp + (tiles - a.dp) * splits : tiles * splits;
     if (grid > 0x7FFFFFFF)
         return TG_ERR_NOT_SUPPORTED;
     constexpr int RB = NtStaging<E>::RB;
@@ -251,6 +299,7 @@ tg_status launch_nt_plan(TileArgs& a, const NtPlan& plan, void* ws, hipStream_t 
 {
     a.group_m = 4;
     a.splits = (uint32_t)plan.splits;
+    a.dp = (uint32_t)plan.dp;
     if (plan.splits > 1) {
         a.counters = (uint32_t*)ws;
         a.partials = (float*)((uint8_t*)ws + kSplitCounterBytes);

@@ -37,6 +37,10 @@ struct TileArgs {
     uint32_t splits;
     uint32_t* counters;
     float* partials;
+    // NT kernel only: with dp > 0 the first dp workgroups run the first dp
+    // tiles of the walk whole, and only the remaining tiles split K `splits`
+    // ways (counters and partial shares are then numbered from tile dp).
+    uint32_t dp;
 };
 
 // B storage: K-contiguous (column-major K x N, i.e. N x K rows) or N-contiguous

@@ -13,11 +13,11 @@ int64_t ex_workspace_bytes(int in, int64_t M, int64_t N, int64_t K, int b_layout
 namespace {
 
 // The scratch: every split plan the library makes needs at most 64 KiB of
-// arrival counters plus 16 MiB of partial tiles (one round of at most 256
-// workgroups, each with a partial tile of at most 128 x 128 fp32), so that is
-// its size.  Each GPU holds its own copy, at its own address, until the
+// arrival counters plus 64 MiB of partial tiles (one round of at most 256
+// split workgroups, each with a partial tile of at most 256 x 256 fp32), so
+// that is its size.  Each GPU holds its own copy, at its own address, until the
 // process ends.
-constexpr int64_t kScratchBytes = (16 << 20) + (64 << 10);
+constexpr int64_t kScratchBytes = (64 << 20) + (64 << 10);
 constexpr int64_t kScratchCounterWords = (64 << 10) / 4;
 
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
