@@ -700,6 +700,42 @@ def test_exact_one_hot_256_tile(tg, dt):
     assert torch.equal(C.cpu(), ref)
 
 
+# The 256 x 128 tile (16-bit inputs, K-contiguous B), which the plan takes
+# for one round of 129 to 256 of its tiles: ragged M and N (partial tiles on
+# both edges), K tails (a partial last K step), every output type; every
+# element against the oracle, and one-hot rows of A (exact).
+def _wide_tiles(M, N):
+    """The plan's condition for the 256 x 128 tile (host logic, restated)."""
+    tw = ((M + 255) // 256) * ((N + 127) // 128)
+    t128 = ((M + 127) // 128) * ((N + 127) // 128)
+    return 128 < tw <= 256 and tw * 8 <= t128 * 5
+
+
+@pytest.mark.parametrize("shape", [(2100, 2200, 1000), (1100, 4000, 520), (2304, 2304, 2304)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_wide_tile(tg, dt, out, shape):
+    M, N, K = shape
+    assert _wide_tiles(M, N)
+    A, B, _, _ = _inputs(dt, M, N, K, "col", seed=M + N + K + 5)
+    C = _run_dense(tg, dt, A, B, "col", out)
+    _check(C, A, B, dt, "col", out)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_wide_tile_one_hot_exact(tg, dt):
+    M, N, K = 2300, 2200, 2056
+    assert _wide_tiles(M, N)
+    Bs = synth.normal((N, K), 905, std=0.05).to(TDT[dt])
+    ks = torch.randint(0, K, (M,), generator=torch.Generator().manual_seed(906))
+    ks[:K] = torch.arange(K)  # every k once
+    A = torch.zeros((M, K))
+    A[torch.arange(M), ks] = 1.0
+    C = _run_dense(tg, dt, A.to(TDT[dt]), Bs, "col", "f32")
+    assert torch.equal(C.cpu(), Bs.float().t()[ks])
+
+
 # One-hot rows of A through the skinny kernel: each output sums one nonzero
 # product over the waves' K ranges, the LDS reduction of their partial
 # tiles and (narrow N, fp32 output) the atomic adds of the workgroups'

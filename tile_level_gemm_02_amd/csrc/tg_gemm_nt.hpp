@@ -127,11 +127,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     static_assert(AI >= 1 && BI >= 1 && (BM / NW) % (RSW * CH) == 0 && (BN / NW) % (RSW * CH) == 0 &&
                   (BM / WM) % (RSW * CH) == 0 && (BN / WN) % (RSW * CH) == 0,
                   "wave row blocks must start on a swizzle period");
-    constexpr int HALF = BM * RB;     // bytes of one half-stage (A and B tiles are square)
+    // one half-stage slot holds the A rows or the B rows of a K step (the
+    // larger of the two: a 256 x 128 tile's B rows fill half of it)
+    constexpr int HALF = (BM > BN ? BM : BN) * RB;
     constexpr int KSTEPS = (E == E_FP8) ? RB / 64 : RB / 32;  // MFMAs along K per step
     static_assert(KSTEPS >= 2 && KSTEPS % 2 == 0, "fragment slots alternate within a step");
-    static_assert(BM == BN && AI == BI, "square tiles: A and B half-stages alike");
-    static_assert(NH >= 4 && (NH - 3) * AI <= 63, "copies in flight");
+    // copy instructions of half-stage h (A rows for even h, B rows for odd h),
+    // and of the half-stages h0 .. h1-1 together (the copy waits below)
+    auto copies_in = [](int h0, int h1) constexpr {
+        int n = 0;
+        for (int h = h0; h < h1; ++h)
+            n += (h & 1) ? BI : AI;
+        return n;
+    };
+    static_assert(NH >= 4 && copies_in(2, NH - 1) <= 63, "copies in flight");
     typedef typename Mfma32<E>::frag Frag;
     // N-contiguous B (row-major K x N): a B half-stage holds the step's KE
     // rows of k, each BN elements wide (RBN bytes, CHN chunks; the same HALF
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     // LDS load (16-bit elements only)
     constexpr bool NB = BL == B_NCONTIG;
     constexpr int RBN = BN * EB, CHN = RBN / 16, RPIN = 1024 / RBN;
-    static_assert(!NB || (KE * RBN == HALF && CHN >= 8 && (KE / RPIN) % NW == 0 && KE / RPIN / NW == BI),
+    static_assert(!NB || (BM == BN && KE * RBN == HALF && CHN >= 8 && (KE / RPIN) % NW == 0 && KE / RPIN / NW == BI),
                   "N-contiguous B stage: same size and copy count as the K-contiguous one");
     // physical chunk of logical chunk c of B row k is c ^ swn(k).  16-bit:
     // the four rows k .. k+3 that one transposing read takes (32 bytes each,
@@ -436,18 +445,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
             if (s == 0)
                 substep(s & 1, rd,
                         [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH - 1, q, p0, p1); },
-                        std::integral_constant<int, AI>{});
+                        std::integral_constant<int, ((NH - 1) & 1) ? BI : AI>{});
             else
                 substep(s & 1, rd, nothing, std::integral_constant<int, 0>{});
         }
         __builtin_amdgcn_sched_barrier(0);
-        wait_copies<(NH - 4) * AI>();  // own copies of step kt+1 landed ...
+        wait_copies<copies_in(4, NH)>();  // own copies of step kt+1 landed ...
         __syncthreads();               // ... and every wave's; the half-stages of step kt are free
         __builtin_amdgcn_sched_barrier(0);
         // (the reads of step kt+1 after the last step are stale and unused)
         substep((KSTEPS - 1) & 1, [&](int r) __attribute__((always_inline)) { read_frag(kt + 1, 0, 0, r); },
                 [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH, q, r0, r1); },
-                std::integral_constant<int, AI>{});
+                std::integral_constant<int, (NH & 1) ? BI : AI>{});
     };
 
     auto run = [&](auto edge) __attribute__((always_inline)) {
@@ -457,10 +466,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
             uint32_t o0, o1;
             half_offs(edge, h, o0, o1);
 #pragma unroll
-            for (int j = 0; j < AI; ++j)
+            for (int j = 0; j < ((h & 1) ? BI : AI); ++j)
                 copy_half(edge, h, j, o0, o1);
         }
-        wait_copies<(NH - 3) * AI>();  // step 0 landed
+        wait_copies<copies_in(2, NH - 1)>();  // step 0 landed
         __syncthreads();
         read_frags(0, 0, 0);
         for (int64_t kt = 0; kt < NK; ++kt)

@@ -180,6 +180,7 @@ struct NtPlan {
     int tile, nh, splits;
     int64_t ws_bytes;  // workspace the plan needs (0 without a split)
     int64_t dp;        // > 0: this many tiles run whole, the rest split `splits` ways
+    int tn;            // the tile's N edge: `tile`, or 128 for the 256 x 128 tile
 };
 
 // Estimated cycles of one compute unit for an NT launch with tile edge T and
@@ -223,11 +224,31 @@ inline double nt_cost(int64_t M, int64_t N, int64_t K, int EB, int T, int S)
     return rounds * nt_round_cost(K, EB, T, S);
 }
 
+// The 256 x 128 tile (4 waves of 128 x 64; 16-bit inputs, K-contiguous B):
+// where it makes one round of more than 128 workgroups, the tiles of
+// 256 x 256 leave compute units idle and those of 128 x 128 need more than a
+// round; unless it pads the output a quarter more than the 128 tile.  Back
+// to back, bf16, against the square tiles' best: 2304^3 48.5 -> 37.1 us,
+// 2560^3 54.6 -> 41.4, 2816^3 60.4 -> 46.7, 2560 x 2560 x 8192 141.5 ->
+// 102.3, 2816 x 2816 x 1024 27.2 -> 21.0, 1024 x 8192 x 4096 76.7 -> 61.9;
+// at 128 of its tiles (2048^3) the 128 tile's one round stays faster (21.4
+// against 31.8 us), and past 256 the 256 tile (3072^3: 64.4 against 90.4).
+template <int EB, int BL>
+inline bool nt_wide(int64_t M, int64_t N)
+{
+    if (EB != 2 || BL != B_KCONTIG)
+        return false;
+    const int64_t tw = n_tiles<256, 128>(M, N), t128 = n_tiles<128, 128>(M, N);
+    return tw > 128 && tw <= 256 && tw * 8 <= t128 * 5;
+}
+
 template <int E, int BL>
 NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
 {
     constexpr int EB = ElemInfo<E>::bytes;
-    NtPlan p{pick_tile_nt<EB>(M, N), 4, 1, 0, 0};
+    if (nt_wide<EB, BL>(M, N))  // (one round of its tiles: a K split would not fit the chip)
+        return NtPlan{256, NtRing<E, 256>::NH, 1, 0, 0, 128};
+    NtPlan p{pick_tile_nt<EB>(M, N), 4, 1, 0, 0, 0};
     if (EB == 1 && BL == B_NCONTIG && p.tile < 128)
         p.tile = 128;  // (nt_eligible_nrow only admits shapes that pick 128 or 256)
     if (allow_split) {
@@ -294,6 +315,7 @@ NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
         p.nh = 8;
     else
         p.nh = tiles * p.splits <= 256 ? 8 : 4;
+    p.tn = p.tile;
     p.ws_bytes = split_ws_bytes(tiles, p.splits, (int64_t)p.tile * p.tile);  // (split tiles only)
     return p;
 }
@@ -322,6 +344,13 @@ tg_status launch_nt_plan(TileArgs& a, const NtPlan& plan, void* ws, hipStream_t 
     if (plan.splits > 1) {
         a.counters = (uint32_t*)ws;
         a.partials = (float*)((uint8_t*)ws + kSplitCounterBytes);
+    }
+    if constexpr (BL == B_KCONTIG) {
+        if (plan.tile == 256 && plan.tn == 128) {
+            if (plan.nh == 5)
+                return launch_nt<E, O, 256, 128, BL, 5>(a, plan.splits, s);
+            return launch_nt<E, O, 256, 128, BL, 4>(a, plan.splits, s);
+        }
     }
     if (plan.tile == 256) {
         if (plan.nh == 5)
