@@ -700,10 +700,10 @@ def test_exact_one_hot_256_tile(tg, dt):
     assert torch.equal(C.cpu(), ref)
 
 
-# The 256 x 128 tile (16-bit inputs, K-contiguous B), which the plan takes
-# for one round of 129 to 256 of its tiles: ragged M and N (partial tiles on
-# both edges), K tails (a partial last K step), every output type; every
-# element against the oracle, and one-hot rows of A (exact).
+# The 256 x 128 tile, which the plan takes for one round of 129 to 256 of
+# its tiles: ragged M and N (partial tiles on both edges), K tails (a
+# partial last K step), every input and output type, both layouts of B;
+# every element against the oracle, and one-hot rows of A (exact).
 def _wide_tiles(M, N):
     """The plan's condition for the 256 x 128 tile (host logic, restated)."""
     tw = ((M + 255) // 256) * ((N + 127) // 128)
@@ -723,17 +723,34 @@ def test_wide_tile(tg, dt, out, shape):
     _check(C, A, B, dt, "col", out)
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
-def test_wide_tile_one_hot_exact(tg, dt):
-    M, N, K = 2300, 2200, 2056
+@pytest.mark.parametrize("dt,lay,out,shape", [
+    ("bf16", "row", "f32", (2100, 2208, 1008)), ("bf16", "row", "bf16", (1100, 4000, 528)),
+    ("f16", "row", "f16", (2304, 2304, 2304)), ("fp8", "col", "bf16", (2100, 2208, 1008)),
+    ("fp8", "row", "f16", (1100, 4000, 528)), ("fp8", "col", "f32", (2304, 2304, 2304)),
+    ("fp8", "row", "f32", (2304, 2304, 2304))], ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_wide_tile_layouts(tg, dt, lay, out, shape):
+    M, N, K = shape
     assert _wide_tiles(M, N)
-    Bs = synth.normal((N, K), 905, std=0.05).to(TDT[dt])
+    A, B, sa, sb = _inputs(dt, M, N, K, lay, seed=M + N + K + 7)
+    C = _run_dense(tg, dt, A, B, lay, out, scale_a=sa, scale_b=sb)
+    _check(C, A, B, dt, lay, out, sa, sb)
+
+
+@pytest.mark.parametrize("dt,lay,shape", [("f16", "col", (2300, 2200, 2056)), ("bf16", "col", (2300, 2200, 2056)),
+                                          ("bf16", "row", (2300, 2208, 2056)), ("fp8", "col", (2300, 2208, 2064)),
+                                          ("fp8", "row", (2300, 2208, 2064))],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_wide_tile_one_hot_exact(tg, dt, lay, shape):
+    M, N, K = shape
+    assert _wide_tiles(M, N)
+    Bs = synth.normal((N, K) if lay == "col" else (K, N), 905, std=0.05).to(TDT[dt])
     ks = torch.randint(0, K, (M,), generator=torch.Generator().manual_seed(906))
     ks[:K] = torch.arange(K)  # every k once
     A = torch.zeros((M, K))
     A[torch.arange(M), ks] = 1.0
-    C = _run_dense(tg, dt, A.to(TDT[dt]), Bs, "col", "f32")
-    assert torch.equal(C.cpu(), Bs.float().t()[ks])
+    C = _run_dense(tg, dt, A.to(TDT[dt]), Bs, lay, "f32")
+    ref = Bs.float().t()[ks] if lay == "col" else Bs.float()[ks]
+    assert torch.equal(C.cpu(), ref)
 
 
 # One-hot rows of A through the skinny kernel: each output sums one nonzero

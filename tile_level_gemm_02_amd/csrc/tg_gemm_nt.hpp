@@ -148,7 +148,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     // LDS load (16-bit elements only)
     constexpr bool NB = BL == B_NCONTIG;
     constexpr int RBN = BN * EB, CHN = RBN / 16, RPIN = 1024 / RBN;
-    static_assert(!NB || (BM == BN && KE * RBN == HALF && CHN >= 8 && (KE / RPIN) % NW == 0 && KE / RPIN / NW == BI),
+    static_assert(!NB || (KE * RBN == BN * RB && CHN >= 8 && (KE / RPIN) % NW == 0 && KE / RPIN / NW == BI),
                   "N-contiguous B stage: same size and copy count as the K-contiguous one");
     // physical chunk of logical chunk c of B row k is c ^ swn(k).  16-bit:
     // the four rows k .. k+3 that one transposing read takes (32 bytes each,

@@ -224,20 +224,20 @@ inline double nt_cost(int64_t M, int64_t N, int64_t K, int EB, int T, int S)
     return rounds * nt_round_cost(K, EB, T, S);
 }
 
-// The 256 x 128 tile (4 waves of 128 x 64; 16-bit inputs, K-contiguous B):
-// where it makes one round of more than 128 workgroups, the tiles of
-// 256 x 256 leave compute units idle and those of 128 x 128 need more than a
-// round; unless it pads the output a quarter more than the 128 tile.  Back
-// to back, bf16, against the square tiles' best: 2304^3 48.5 -> 37.1 us,
-// 2560^3 54.6 -> 41.4, 2816^3 60.4 -> 46.7, 2560 x 2560 x 8192 141.5 ->
-// 102.3, 2816 x 2816 x 1024 27.2 -> 21.0, 1024 x 8192 x 4096 76.7 -> 61.9;
-// at 128 of its tiles (2048^3) the 128 tile's one round stays faster (21.4
-// against 31.8 us), and past 256 the 256 tile (3072^3: 64.4 against 90.4).
+// The 256 x 128 tile (4 waves of 128 x 64): where it makes one round of
+// more than 128 workgroups, the tiles of 256 x 256 leave compute units idle
+// and those of 128 x 128 need more than a round; unless it pads the output a
+// quarter more than the 128 tile.  Back to back, against the square tiles'
+// best: bf16 2304^3 48.5 -> 37.1 us, 2560^3 54.6 -> 41.4, 2816^3 60.4 ->
+// 46.7, 2816 x 2816 x 1024 27.2 -> 21.0, 1024 x 8192 x 4096 76.7 -> 61.9
+// (B row-major alike: 2560^3 52.9 -> 39.8); fp8 2304^3 30.1 -> 21.0,
+// 2304 x 2304 x 8192 89.1 -> 54.5, 1536 x 3072 x 4096 47.4 -> 30.6 (B
+// row-major alike).  At 128 of its tiles (2048^3) the 128 tile's one round
+// stays faster (bf16 21.4 against 31.8 us), and past 256 the 256 tile
+// (3072^3: 64.4 against 90.4).
 template <int EB, int BL>
 inline bool nt_wide(int64_t M, int64_t N)
 {
-    if (EB != 2 || BL != B_KCONTIG)
-        return false;
     const int64_t tw = n_tiles<256, 128>(M, N), t128 = n_tiles<128, 128>(M, N);
     return tw > 128 && tw <= 256 && tw * 8 <= t128 * 5;
 }
@@ -345,12 +345,10 @@ tg_status launch_nt_plan(TileArgs& a, const NtPlan& plan, void* ws, hipStream_t 
         a.counters = (uint32_t*)ws;
         a.partials = (float*)((uint8_t*)ws + kSplitCounterBytes);
     }
-    if constexpr (BL == B_KCONTIG) {
-        if (plan.tile == 256 && plan.tn == 128) {
-            if (plan.nh == 5)
-                return launch_nt<E, O, 256, 128, BL, 5>(a, plan.splits, s);
-            return launch_nt<E, O, 256, 128, BL, 4>(a, plan.splits, s);
-        }
+    if (plan.tile == 256 && plan.tn == 128) {
+        if (plan.nh == 5)
+            return launch_nt<E, O, 256, 128, BL, 5>(a, plan.splits, s);
+        return launch_nt<E, O, 256, 128, BL, 4>(a, plan.splits, s);
     }
     if (plan.tile == 256) {
         if (plan.nh == 5)
