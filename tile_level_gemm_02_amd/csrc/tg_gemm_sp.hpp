@@ -62,13 +62,16 @@ __device__ __forceinline__ void load_lds_256_at(i32x4_t r, uint32_t dst, uint32_
                  : "memory");
 }
 
-constexpr int kSpThreads = 512;
-
-template <int O, bool CP4>
-__global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
+// Waves per workgroup: 8 (2 x 4, each 128 x 64) or 4 (2 x 2, each 128 x 128).
+// The copies are laid out for 8 copy slots of 32 rows each; with 4 waves each
+// wave issues the copies of two slots.
+template <int O, bool CP4, int NW = 8>
+__global__ __launch_bounds__(64 * NW) void gemm_sp24(SpArgs p)
 {
-    constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NW = WM * WN;
-    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 4 x 2 blocks of 32 x 32 per wave
+    static_assert(NW == 8 || NW == 4, "8 or 4 waves");
+    constexpr int BM = 256, BN = 256, WM = 2, WN = NW / 2;
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 4 x 2 (8 waves) or 4 x 4 blocks of 32 x 32 per wave
+    constexpr int VPW = 8 / NW;                          // copy slots per wave
     constexpr int KE = 64;                              // dense k per step
     constexpr int AB = BM * 128, VB = BN * 64, MB = CP4 ? 0 : BN * 8;
     constexpr int STAGE = AB + VB + MB;
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
     constexpr int CPB = BN * 32;               // codes of a 4-step period (CP4)
     constexpr int CODES = NS * STAGE;          // offset of the two code periods (CP4)
     constexpr int BYTES = NS * STAGE + (CP4 ? 2 * CPB : 0);
-    constexpr int PER = 4 + 2 + 1;  // copy instructions per wave per step: A rows, values, codes
+    constexpr int PER = 4 + 2 + 1;  // copy instructions per slot per step: A rows, values, codes
     static_assert(BYTES <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[BYTES];
 
@@ -97,54 +100,62 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
     const int64_t KT = K / KE;  // K is a multiple of KE
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
 
-    // ---- copy lanes.  A: instruction j covers rows 32w + 8j .. +7 (lane/8),
+    // ---- copy lanes (copy slot w = VPW * wave + v; the slot's row offset
+    // 32v joins the scalar offset).  A: instruction j covers rows 32w + 8j .. +7 (lane/8),
     // physical chunk lane%8 holding logical chunk (lane%8) ^ ((row/2)%8): one
     // value for even j, one for odd j.  Values: instruction j covers rows
     // 32w + 16j .. +15 (lane/4), physical chunk lane%4 holding logical chunk
     // (lane%4) ^ ((row/4)%4).  Codes: rows 32w .. +31 (lane/2), dword lane%2.
-    const uint32_t arow = wave * 32u + lane / 8u;
+    const uint32_t slot0 = wave * VPW;  // first copy slot of this wave
+    const uint32_t arow = slot0 * 32u + lane / 8u;
     const uint32_t ach0 = (lane % 8u) ^ ((lane / 16u) % 8u);
     const uint32_t ach1 = (lane % 8u) ^ ((4u + lane / 16u) % 8u);
-    const uint32_t vrow = wave * 32u + lane / 4u;
+    const uint32_t vrow = slot0 * 32u + lane / 4u;
     const uint32_t vch = (lane % 4u) ^ ((lane / 16u) % 4u);
-    const uint32_t mrow = wave * 32u + lane / 2u;
+    const uint32_t mrow = slot0 * 32u + lane / 2u;
     const uint32_t va0 = arow * ldab + ach0 * 16u, va1 = arow * ldab + ach1 * 16u;
     const uint32_t vv = vrow * ldvb + vch * 16u;
     const uint32_t vm = mrow * ldmb + (lane % 2u) * 4u;
     // CP4: lane l copies the codes of row 32w + l%32 for step pair l/32 of a period
-    const uint32_t crow = wave * 32u + lane % 32u, cpair = lane / 32u;
+    const uint32_t crow = slot0 * 32u + lane % 32u, cpair = lane / 32u;
     const uint32_t vc = crow * ldmb + cpair * 16u;
 
-    // copy instruction q (0 .. PER-1) of step kt into the stage at byte offset `so`
-    auto copy = [&](auto edge, int64_t kt, uint32_t so, int q) __attribute__((always_inline)) {
+    // copy instruction qs (0 .. VPW*PER-1) of step kt into the stage at byte
+    // offset `so`: instruction q = qs % PER of copy slot slot0 + qs / PER
+    auto copy = [&](auto edge, int64_t kt, uint32_t so, int qs) __attribute__((always_inline)) {
+        const int sv = qs / PER, q = qs % PER;
+        const uint32_t sw32 = (uint32_t)sv * 32u;  // row offset of the slot past slot0
+        const uint32_t sl = slot0 + (uint32_t)sv;   // the copy slot
         const uint32_t past = kt < KT ? 0u : kOutOfRange;
         const uint32_t base = lds0 + so;
         if (q < 4) {
             uint32_t v = ((q & 1) ? va1 : va0) | past;
             if constexpr (decltype(edge)::value)
-                v |= (int32_t)(arow + 8u * q) < rows_a ? 0u : kOutOfRange;
-            load_lds_1k_at(ra, base + wave * 4096u + q * 1024u, v, (uint32_t)kt * 128u + (uint32_t)(8 * q) * ldab);
+                v |= (int32_t)(arow + sw32 + 8u * q) < rows_a ? 0u : kOutOfRange;
+            load_lds_1k_at(ra, base + sl * 4096u + q * 1024u, v,
+                           (uint32_t)kt * 128u + (uint32_t)(8 * q) * ldab + sw32 * ldab);
         } else if (q < 6) {
             const int j = q - 4;
             uint32_t v = vv | past;
             if constexpr (decltype(edge)::value)
-                v |= (int32_t)(vrow + 16u * j) < rows_w ? 0u : kOutOfRange;
-            load_lds_1k_at(rv, base + AB + wave * 2048u + j * 1024u, v,
-                           (uint32_t)kt * 64u + (uint32_t)(16 * j) * ldvb);
+                v |= (int32_t)(vrow + sw32 + 16u * j) < rows_w ? 0u : kOutOfRange;
+            load_lds_1k_at(rv, base + AB + sl * 2048u + j * 1024u, v,
+                           (uint32_t)kt * 64u + (uint32_t)(16 * j) * ldvb + sw32 * ldvb);
         } else if constexpr (!CP4) {
             uint32_t v = vm | past;
             if constexpr (decltype(edge)::value)
-                v |= (int32_t)mrow < rows_w ? 0u : kOutOfRange;
-            load_lds_256_at(rm, base + AB + VB + wave * 256u, v, (uint32_t)kt * 8u);
+                v |= (int32_t)(mrow + sw32) < rows_w ? 0u : kOutOfRange;
+            load_lds_256_at(rm, base + AB + VB + sl * 256u, v, (uint32_t)kt * 8u + sw32 * ldmb);
         } else if ((kt & 3) == 0) {  // CP4: the codes of steps kt .. kt+3 (pairs past K read zeros)
             uint32_t v = vc | (kt + 2 * (int64_t)cpair < KT ? 0u : kOutOfRange);
             if constexpr (decltype(edge)::value)
-                v |= (int32_t)crow < rows_w ? 0u : kOutOfRange;
-            load_lds_1k_at(rm, lds0 + CODES + (uint32_t)((kt >> 2) & 1) * CPB + wave * 1024u, v, (uint32_t)kt * 8u);
+                v |= (int32_t)(crow + sw32) < rows_w ? 0u : kOutOfRange;
+            load_lds_1k_at(rm, lds0 + CODES + (uint32_t)((kt >> 2) & 1) * CPB + sl * 1024u, v,
+                           (uint32_t)kt * 8u + sw32 * ldmb);
         }
     };
-    // copy instructions in the batch of step kt (the wait counts below)
-    auto batch = [&](int64_t kt) __attribute__((always_inline)) { return CP4 && (kt & 3) != 0 ? PER - 1 : PER; };
+    // copy instructions of this wave in the batch of step kt (the wait counts below)
+    auto batch = [&](int64_t kt) __attribute__((always_inline)) { return VPW * (CP4 && (kt & 3) != 0 ? PER - 1 : PER); };
 
     // ---- fragments.  Every row a lane reads has the same swizzle.
     const uint32_t wm = wave / WN, wn = wave % WN;
@@ -224,25 +235,25 @@ __global__ __launch_bounds__(kSpThreads) void gemm_sp24(SpArgs p)
         substep(0, [&](int r) __attribute__((always_inline)) { read_frag(cur, kt, 1, 1, r); }, nothing,
                 std::integral_constant<int, 0>{});
         __builtin_amdgcn_sched_barrier(0);
-        if (batch(kt + 2) == PER)  // step kt+1 landed (step kt+2 may be in flight)
-            wait_copies<PER>();
+        if (batch(kt + 2) == VPW * PER)  // step kt+1 landed (step kt+2 may be in flight)
+            wait_copies<VPW * PER>();
         else
-            wait_copies<PER - 1>();
+            wait_copies<VPW * (PER - 1)>();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         // (the reads of step kt+1 after the last step are stale and unused)
         substep(1, [&](int r) __attribute__((always_inline)) { read_frag(nxt, kt + 1, 0, 0, r); },
                 [&](int q) __attribute__((always_inline)) { copy(edge, kt + NS, cur, q); },
-                std::integral_constant<int, PER>{});
+                std::integral_constant<int, VPW * PER>{});
     };
     auto run = [&](auto edge) __attribute__((always_inline)) {
 #pragma unroll
         for (int st = 0; st < NS; ++st)
 #pragma unroll
-            for (int q = 0; q < PER; ++q)
+            for (int q = 0; q < VPW * PER; ++q)
                 copy(edge, st, (uint32_t)(st * STAGE), q);
         static_assert(NS == 3, "the prologue wait counts steps 1 and 2");
-        wait_copies<CP4 ? 2 * (PER - 1) : 2 * PER>();  // step 0 landed (steps 1, 2 may be in flight)
+        wait_copies<VPW * (CP4 ? 2 * (PER - 1) : 2 * PER)>();  // step 0 landed (steps 1, 2 may be in flight)
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < NR; ++r)

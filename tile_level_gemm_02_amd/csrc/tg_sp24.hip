@@ -13,18 +13,26 @@ bool sp24_offsets_fit(int64_t K, int64_t lda, int64_t ldv, int64_t ldm)
     return 256 * lda * 2 + K * 2 < lim && 256 * ldv * 2 + K < lim && 256 * ldm + K / 8 < lim;
 }
 
+// Waves per workgroup of gemm_sp24: 8.  Four (128 x 128 per wave, each
+// wave issuing two copy slots' copies) gave bit-identical results but ran
+// slower at every shape tried, interleaved on one lease: 4096^3 82.8 ->
+// 108.9 us, 8192^3 571 -> 636, 2304^3 37.6 -> 48.5, 4100 x 4000 x 4160
+// 146 -> 153.
+constexpr int kSpWaves = 8;
+
 template <bool CP4>
 tg_status launch_sp24(const tg::SpArgs& a, int c_dtype, int64_t tiles, hipStream_t s)
 {
+    constexpr int W = kSpWaves;
     switch (c_dtype) {
     case TG_F32:
-        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_F32, CP4>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
+        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_F32, CP4, W>), dim3((uint32_t)tiles), dim3(64 * W), 0, s, a);
         break;
     case TG_F16:
-        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_F16, CP4>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
+        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_F16, CP4, W>), dim3((uint32_t)tiles), dim3(64 * W), 0, s, a);
         break;
     default:
-        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_BF16, CP4>), dim3((uint32_t)tiles), dim3(tg::kSpThreads), 0, s, a);
+        hipLaunchKernelGGL((tg::gemm_sp24<tg::O_BF16, CP4, W>), dim3((uint32_t)tiles), dim3(64 * W), 0, s, a);
         break;
     }
     return tg::launched();
