@@ -330,6 +330,8 @@ def main():
                           "launches": args.steps}), flush=True)
         return
     flush = make_flush()
+    flush()  # its first call loads the reduction kernel (≈24 ms): not between the warm-up and the timed steps
+    torch.cuda.synchronize()
     if args.only:
         setup = {"bf16_4096": setup_bf16_4096, "bf16_skinny": setup_skinny, "bf16_skinny_n1024": setup_skinny_shard,
                  "bf16_skinny_n1024_ws": lambda: setup_skinny_shard(True), "fp8_8192": setup_fp8, "fp8_8192_rowb": setup_fp8_rowb,
