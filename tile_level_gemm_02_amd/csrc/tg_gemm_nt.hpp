@@ -127,9 +127,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     static_assert(AI >= 1 && BI >= 1 && (BM / NW) % (RSW * CH) == 0 && (BN / NW) % (RSW * CH) == 0 &&
                   (BM / WM) % (RSW * CH) == 0 && (BN / WN) % (RSW * CH) == 0,
                   "wave row blocks must start on a swizzle period");
-    // one half-stage slot holds the A rows or the B rows of a K step (the
-    // larger of the two: a 256 x 128 tile's B rows fill half of it)
+    // One half-stage slot holds the A rows or the B rows of a K step.  With an
+    // even ring depth half-stage h always lands in a slot of h's parity, so
+    // the A slots (even) and B slots (odd) take their own sizes (a 256 x 128
+    // tile: 32 and 16 KiB, six half-stages in 144 KiB); with an odd depth
+    // every slot takes the larger size.
+    constexpr int ASZ = BM * RB, BSZ = BN * RB;
     constexpr int HALF = (BM > BN ? BM : BN) * RB;
+    constexpr int LDS_BYTES = NH % 2 == 0 ? NH / 2 * (ASZ + BSZ) : NH * HALF;
+    static_assert(NH % 2 == 0 || BM == BN, "odd ring depths take square tiles");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    // byte offset of half-stage h's slot
+    auto slot_of = [](int64_t h) __attribute__((always_inline)) -> uint32_t {
+        const uint32_t i = (uint32_t)h % (uint32_t)NH;  // (h >= 0, below 2^31)
+        if constexpr (NH % 2 == 0)
+            return (i / 2u) * (uint32_t)(ASZ + BSZ) + (i & 1u) * (uint32_t)ASZ;
+        else
+            return i * (uint32_t)HALF;
+    };
     constexpr int KSTEPS = (E == E_FP8) ? RB / 64 : RB / 32;  // MFMAs along K per step
     static_assert(KSTEPS >= 2 && KSTEPS % 2 == 0, "fragment slots alternate within a step");
     // copy instructions of half-stage h (A rows for even h, B rows for odd h),
@@ -170,7 +185,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         }
     };
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[NH * HALF];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases scalar
@@ -250,10 +265,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
 
     // half-stage of A (or B) of K step kt
     auto a_ptr = [&](int64_t kt) __attribute__((always_inline)) -> uint8_t* {
-        return lds + (uint32_t)((2 * kt) % NH) * HALF;
+        return lds + slot_of(2 * kt);
     };
     auto b_ptr = [&](int64_t kt) __attribute__((always_inline)) -> uint8_t* {
-        return lds + (uint32_t)((2 * kt + 1) % NH) * HALF;
+        return lds + slot_of(2 * kt + 1);
     };
     auto chunk_oob = [&](int64_t kt, uint32_t lchunk) __attribute__((always_inline)) -> uint32_t {
         // a chunk at or past K (only in the last step) reads through an
@@ -284,7 +299,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     // LDS address of this wave's rows in half-stage h
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
     auto half_dst = [&](int64_t h) __attribute__((always_inline)) -> uint32_t {
-        return lds0 + (uint32_t)(h % NH) * HALF + wave * ((h & 1) ? BN / NW : BM / NW) * RB;
+        return lds0 + slot_of(h) + wave * ((h & 1) ? BN / NW : BM / NW) * RB;
     };
     // copy instruction q of half-stage h (A of step h/2 for even h, B for odd
     // h), with the offsets o0/o1 of that half-stage
@@ -594,7 +609,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         // so it goes in passes of PR rows.
         constexpr int OB = WC * 4;            // bytes per staged output row
         constexpr int NCH = OB / 16;          // 16-byte chunks per row
-        constexpr int PBY = NH * HALF / NW;   // staging bytes per wave
+        constexpr int PBY = LDS_BYTES / NW;   // staging bytes per wave
         // rows per pass: the largest of WR, WR/2, WR/4 that fits
         constexpr int PR = PBY / OB >= WR ? WR : (PBY / OB >= WR / 2 ? WR / 2 : WR / 4);
         static_assert(PR % 32 == 0 && WR % PR == 0 && (PR * NCH) % 64 == 0, "fp32 staging passes");
@@ -643,7 +658,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
         constexpr int OB = WC * 2;          // bytes per staged output row
         constexpr int NCH = OB / 16;        // 16-byte chunks per row
         constexpr int WBYTES = WR * OB;     // bytes per wave
-        static_assert(NW * WBYTES <= NH * HALF, "epilogue staging must fit the stage buffers");
+        static_assert(NW * WBYTES <= LDS_BYTES, "epilogue staging must fit the stage buffers");
         uint8_t* ep = lds + wave * WBYTES;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {

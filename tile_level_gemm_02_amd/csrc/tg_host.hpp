@@ -242,6 +242,10 @@ inline double nt_cost(int64_t M, int64_t N, int64_t K, int EB, int T, int S)
 // row-major alike).  At 128 of its tiles (2048^3) the 128 tile's one round
 // stays faster (bf16 21.4 against 31.8 us), and past 256 the 256 tile
 // (3072^3: 64.4 against 90.4).
+// Ring depth of the 256 x 128 tile: six half-stages (three K steps in
+// flight; its A and B slots of 32 and 16 KiB take 144 KiB).
+constexpr int kWideNH = 6;
+
 template <int EB, int BL>
 inline bool nt_wide(int64_t M, int64_t N)
 {
@@ -254,7 +258,7 @@ NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
 {
     constexpr int EB = ElemInfo<E>::bytes;
     if (nt_wide<EB, BL>(M, N))  // (one round of its tiles: a K split would not fit the chip)
-        return NtPlan{256, NtRing<E, 256>::NH, 1, 0, 0, 128};
+        return NtPlan{256, kWideNH, 1, 0, 0, 128};
     NtPlan p{pick_tile_nt<EB>(M, N), 4, 1, 0, 0, 0};
     if (EB == 1 && BL == B_NCONTIG && p.tile < 128)
         p.tile = 128;  // (nt_eligible_nrow only admits shapes that pick 128 or 256)
@@ -353,8 +357,8 @@ tg_status launch_nt_plan(TileArgs& a, const NtPlan& plan, void* ws, hipStream_t 
         a.partials = (float*)((uint8_t*)ws + kSplitCounterBytes);
     }
     if (plan.tile == 256 && plan.tn == 128) {
-        if (plan.nh == 5)
-            return launch_nt<E, O, 256, 128, BL, 5>(a, plan.splits, s);
+        if (plan.nh == 6)
+            return launch_nt<E, O, 256, 128, BL, 6>(a, plan.splits, s);
         return launch_nt<E, O, 256, 128, BL, 4>(a, plan.splits, s);
     }
     if (plan.tile == 256) {
