@@ -144,13 +144,24 @@ inline bool nt_eligible_nrow(const TileArgs& a)
 }
 
 // Staging of the NT kernel: bytes of K per staged row, and LDS half-stages in
-// the ring.  For 16-bit inputs four (two full stages) measured faster than
-// five on the 256 x 256 tile at 4096^3 (the fifth fills the LDS: 5 x 32 KB);
-// fp8 at 8192^3, whose copies miss L2 more often and wait longer, runs ~9%
-// faster with the fifth.
+// the ring of the 256 x 256 tile.  fp8 takes five (2.5 K steps in flight:
+// its copies miss L2 more often and wait longer; ~9% faster at 8192^3).  For
+// 16-bit inputs five (all 160 KiB of LDS) against four: with the operands
+// outside the Infinity Cache (flushed launches) five ran 2-14% faster —
+// 3072^3 76.5 -> 65.9 us, 3584^3 91.3 -> 82.3, 4096^3 111.2 -> 108.5 — but
+// back to back (operands cached) 1-2% slower: 4096^3 102.4 -> 104.2, 8192^3
+// 773 -> 783.  A launch of fewer than 256 tiles runs in one round, all of it
+// on cold operands when they come from HBM, so it takes five; a full round
+// or more (4096^3 and up, where later rounds find the operands cached)
+// keeps four.
 template <int E> struct NtStaging { static constexpr int RB = 128; };
 template <int E, int BM> struct NtRing { static constexpr int NH = 4; };
 template <> struct NtRing<E_FP8, 256> { static constexpr int NH = 5; };
+template <int E>
+inline int nt_ring256(int64_t tiles)
+{
+    return E == E_FP8 || tiles < 256 ? 5 : NtRing<E, 256>::NH;
+}
 
 // Waves of the NT kernel per tile: the 256 x 256 tile takes 8 (2 x 4, two
 // per SIMD) for the LDS read rate its fragments need; smaller tiles take 4.
@@ -321,7 +332,7 @@ NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
     // waits on copy latency: at N = K = 8192, M = 128 (64 tiles) 96 -> 45 us,
     // M = 256 (128 tiles) 114 -> 77 us; 2048^3 27 -> 21 us.
     if (p.tile == 256)
-        p.nh = E == E_FP8 ? NtRing<E_FP8, 256>::NH : NtRing<E, 256>::NH;
+        p.nh = p.dp > 0 ? nt_ring256<E>(tiles + p.dp) : nt_ring256<E>(tiles);
     else if (p.tile == 64)
         p.nh = 8;
     else
