@@ -195,6 +195,27 @@ def setup_bf16_m256(split: bool):
     return w, fn, 2.0 * M * N * K, 2 * (M * K + N * K + M * N)
 
 
+def setup_bf16_4608(split: bool):
+    """bf16 4608^3 (324 tiles of 256 x 256: a second round of 68 tiles on 256
+    compute units), bf16 out: the plain entry point, or tg_gemm_ex with a
+    workspace (the last round's tiles split K behind the whole ones)."""
+    import torch
+    import synth
+    import tile_level_gemm_02_amd as tg
+
+    w = synth.workload("bf16_4096", M=4608, N=4608, K=4608)
+    A, B = w["A"].cuda(), w["B"].cuda()
+    C = torch.empty((w["M"], w["N"]), dtype=torch.bfloat16, device="cuda")
+    if split:
+        need = tg.tg_gemm_ex_workspace_bytes(torch.bfloat16, w["M"], w["N"], w["K"])
+        ws = torch.zeros(max(need, 256) // 4, dtype=torch.int32, device="cuda")
+        fn = lambda: tg.tg_gemm_ex(A, B, C, b_layout="col", workspace=ws)
+    else:
+        fn = lambda: tg.tg_gemm_bf16(A, B, C, b_layout="col")
+    M, N, K = w["M"], w["N"], w["K"]
+    return w, fn, 2.0 * M * N * K, 2 * (M * K + N * K + M * N)
+
+
 def setup_fp8_rowb():
     """The fp8 workload with B stored row-major (K x N): transposing LDS reads."""
     import torch
@@ -411,6 +432,8 @@ def main():
                                       ("w4a16_m1", lambda: setup_w4a16(1), "hbm"),
                                       ("bf16_m256", lambda: setup_bf16_m256(False), "mfma"),
                                       ("bf16_m256_split", lambda: setup_bf16_m256(True), "mfma"),
+                                      ("bf16_4608", lambda: setup_bf16_4608(False), "mfma"),
+                                      ("bf16_4608_split", lambda: setup_bf16_4608(True), "mfma"),
                                       ("fp8_8192_rowb", setup_fp8_rowb, "fp8"),
                                       ("sp24_4096", setup_sp24, "sp")):
             w2, fn2, fl2, by2 = setup()
