@@ -753,6 +753,44 @@ def test_wide_tile_one_hot_exact(tg, dt, lay, shape):
     assert torch.equal(C.cpu(), ref)
 
 
+# More than one round of 256 x 256 tiles with a short last round, through
+# the plain entry points: the first 256 tiles of the walk run whole and the
+# rest as 256 x 128 column halves in a second launch.  4300 x 4100: 289
+# tiles, the last round 33 of them, among them the bottom row of tiles (204
+# rows) and the right-edge tiles 4 columns wide (their right halves empty).
+def _tail_tiles(M, N):
+    """(tiles of 256 x 256, tiles of the short last round) (host logic, restated)."""
+    t = ((M + 255) // 256) * ((N + 255) // 256)
+    return t, t % 256
+
+
+@pytest.mark.parametrize("dt,lay,out,shape", [
+    ("bf16", "col", "bf16", (4300, 4100, 1032)), ("f16", "row", "f32", (4300, 4104, 520)),
+    ("fp8", "col", "bf16", (4300, 4112, 1040)), ("bf16", "col", "f32", (4352, 4352, 272))],
+    ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_short_last_round_plain(tg, dt, lay, out, shape):
+    M, N, K = shape
+    tiles, R = _tail_tiles(M, N)
+    assert tiles > 256 and 0 < R <= 128
+    A, B, sa, sb = _inputs(dt, M, N, K, lay, seed=M + N + K + 13)
+    C = _run_dense(tg, dt, A, B, lay, out, scale_a=sa, scale_b=sb)
+    _check(C, A, B, dt, lay, out, sa, sb)
+
+
+@pytest.mark.parametrize("dt,lay", [("bf16", "col"), ("fp8", "col"), ("bf16", "row"), ("fp8", "row")])
+def test_short_last_round_plain_one_hot_exact(tg, dt, lay):
+    M, N, K = 4300, 4112, 2064
+    assert 0 < _tail_tiles(M, N)[1] <= 128
+    Bs = synth.normal((N, K) if lay == "col" else (K, N), 907, std=0.05).to(TDT[dt])
+    ks = torch.randint(0, K, (M,), generator=torch.Generator().manual_seed(908))
+    ks[:K] = torch.arange(K)  # every k once
+    A = torch.zeros((M, K))
+    A[torch.arange(M), ks] = 1.0
+    C = _run_dense(tg, dt, A.to(TDT[dt]), Bs, lay, "f32")
+    ref = Bs.float().t()[ks] if lay == "col" else Bs.float()[ks]
+    assert torch.equal(C.cpu(), ref)
+
+
 # One-hot rows of A through the skinny kernel: each output sums one nonzero
 # product over the waves' K ranges, the LDS reduction of their partial
 # tiles and (narrow N, fp32 output) the atomic adds of the workgroups'

@@ -200,8 +200,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     // that a last round of few tiles still fills the compute units; split
     // tiles are numbered from p.dp (`stile`) for their counters and shares.
     uint32_t S = p.splits > 1u ? p.splits : 1u;
-    uint32_t tmi, tni, ks = 0u, stile;
-    if (p.dp == 0u) {
+    uint32_t tmi, tni, ks = 0u, stile = 0u;
+    if (BM == 2 * BN && p.sub256 != 0u) {
+        // column halves of the 256 x 256 tiles from walk position sub256 - 1 on
+        const uint32_t tm2 = (uint32_t)((M + 2 * BN - 1) / (2 * BN)), tn2 = (uint32_t)((N + 2 * BN - 1) / (2 * BN));
+        const uint32_t j = xcd_remap(blockIdx.x, gridDim.x);
+        uint32_t tn_2;
+        group_walk(p.sub256 - 1u + j / 2u, tm2, tn2, p.group_m, tmi, tn_2);
+        tni = 2u * tn_2 + (j & 1u);
+        S = 1u;
+        if ((int64_t)tni * BN >= N)
+            return;  // (the right half of a tile at the right edge that is narrower than 128 + 1 columns)
+    } else if (p.dp == 0u) {
         tile_split_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, S, p.group_m, tmi, tni, ks);
         stile = tmi * tiles_n + tni;
     } else if (blockIdx.x < p.dp) {

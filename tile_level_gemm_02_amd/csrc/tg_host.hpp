@@ -199,6 +199,7 @@ struct NtPlan {
     int64_t ws_bytes;  // workspace the plan needs (0 without a split)
     int64_t dp;        // > 0: this many tiles run whole, the rest split `splits` ways
     int tn;            // the tile's N edge: `tile`, or 128 for the 256 x 128 tile
+    bool tail_wide;    // 256 tile: the first dp tiles whole, then the rest as 256 x 128 halves
 };
 
 // Estimated cycles of one compute unit for an NT launch with tile edge T and
@@ -269,8 +270,8 @@ NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
 {
     constexpr int EB = ElemInfo<E>::bytes;
     if (nt_wide<EB, BL>(M, N))  // (one round of its tiles: a K split would not fit the chip)
-        return NtPlan{256, kWideNH, 1, 0, 0, 128};
-    NtPlan p{pick_tile_nt<EB>(M, N), 4, 1, 0, 0, 0};
+        return NtPlan{256, kWideNH, 1, 0, 0, 128, false};
+    NtPlan p{pick_tile_nt<EB>(M, N), 4, 1, 0, 0, 0, false};
     if (EB == 1 && BL == B_NCONTIG && p.tile < 128)
         p.tile = 128;  // (nt_eligible_nrow only admits shapes that pick 128 or 256)
     if (allow_split) {
@@ -322,6 +323,17 @@ NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
             }
         }
     }
+    // A short last round without a split: its tiles run as 256 x 128 column
+    // halves in a second launch (each half about half a tile's time), so the
+    // round takes about half as long; no workspace is needed.
+    if (p.tile == 256 && p.splits == 1) {
+        const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+        const int64_t D = tiles256 / 256 * 256, R = tiles256 - D;
+        if (D > 0 && R > 0 && R * 2 <= 256) {
+            p.tail_wide = true;
+            p.dp = D;
+        }
+    }
     const int64_t tiles = p.dp > 0 ? ((M + 255) / 256) * ((N + 255) / 256) - p.dp
                                    : ((M + p.tile - 1) / p.tile) * ((N + p.tile - 1) / p.tile);
     // ring depth: the 256 tile per element type; the 128 and 64 tiles take 8
@@ -343,10 +355,10 @@ NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
 }
 
 template <int E, int O, int BM, int BN, int BL, int NH>
-tg_status launch_nt(const TileArgs& a, int splits, hipStream_t s)
+tg_status launch_nt(const TileArgs& a, int splits, hipStream_t s, int64_t grid_override = 0)
 {
     const int64_t tiles = n_tiles<BM, BN>(a.M, a.N);
-    const int64_t grid = a.dp > 0 ? a.dp + (tiles - a.dp) * splits : tiles * splits;
+    const int64_t grid = grid_override > 0 ? grid_override : a.dp > 0 ? a.dp + (tiles - a.dp) * splits : tiles * splits;
     if (grid > 0x7FFFFFFF)
         return TG_ERR_NOT_SUPPORTED;
     constexpr int RB = NtStaging<E>::RB;
@@ -366,6 +378,21 @@ tg_status launch_nt_plan(TileArgs& a, const NtPlan& plan, void* ws, hipStream_t 
     if (plan.splits > 1) {
         a.counters = (uint32_t*)ws;
         a.partials = (float*)((uint8_t*)ws + kSplitCounterBytes);
+    }
+    if (plan.tail_wide) {
+        // the first plan.dp tiles of 256 x 256 whole, then every other tile of
+        // the walk as two column halves of 256 x 128, in a second launch
+        const int64_t tiles = n_tiles<256, 256>(a.M, a.N);
+        TileArgs b = a;
+        a.dp = (uint32_t)plan.dp;
+        tg_status st = plan.nh == 5 ? launch_nt<E, O, 256, 256, BL, 5>(a, 1, s, plan.dp)
+                                    : launch_nt<E, O, 256, 256, BL, 4>(a, 1, s, plan.dp);
+        if (st != TG_OK)
+            return st;
+        b.dp = 0;
+        b.splits = 1;
+        b.sub256 = (uint32_t)plan.dp + 1u;
+        return launch_nt<E, O, 256, 128, BL, kWideNH>(b, 1, s, 2 * (tiles - plan.dp));
     }
     if (plan.tile == 256 && plan.tn == 128) {
         if (plan.nh == 6)

@@ -41,6 +41,11 @@ struct TileArgs {
     // tiles of the walk whole, and only the remaining tiles split K `splits`
     // ways (counters and partial shares are then numbered from tile dp).
     uint32_t dp;
+    // NT kernel with 256 x 128 tiles only: with sub256 > 0, workgroup j
+    // covers column half j % 2 of the 256 x 256 tile at position
+    // sub256 - 1 + j / 2 of the 256 x 256 walk (the tiles that a 256 x 256
+    // launch of the first sub256 - 1 tiles left over).
+    uint32_t sub256;
 };
 
 // B storage: K-contiguous (column-major K x N, i.e. N x K rows) or N-contiguous
