@@ -201,16 +201,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
     // tiles are numbered from p.dp (`stile`) for their counters and shares.
     uint32_t S = p.splits > 1u ? p.splits : 1u;
     uint32_t tmi, tni, ks = 0u, stile = 0u;
-    if (BM == 2 * BN && p.sub256 != 0u) {
-        // column halves of the 256 x 256 tiles from walk position sub256 - 1 on
-        const uint32_t tm2 = (uint32_t)((M + 2 * BN - 1) / (2 * BN)), tn2 = (uint32_t)((N + 2 * BN - 1) / (2 * BN));
+    constexpr bool SUB = BM < 256 || BN < 256;  // (a tile smaller than 256 x 256 can cover parts of one)
+    if (SUB && p.sub256 != 0u) {
+        // the QM x QN parts of the 256 x 256 tiles from walk position
+        // sub256 - 1 on: workgroup j takes part j % Q of tile sub256 - 1 + j / Q
+        constexpr uint32_t QM = 256 / BM, QN = 256 / BN, Q = QM * QN;
+        static_assert(QM * BM == 256 && QN * BN == 256, "parts of a 256 x 256 tile");
+        const uint32_t tm2 = (uint32_t)((M + 255) / 256), tn2 = (uint32_t)((N + 255) / 256);
         const uint32_t j = xcd_remap(blockIdx.x, gridDim.x);
-        uint32_t tn_2;
-        group_walk(p.sub256 - 1u + j / 2u, tm2, tn2, p.group_m, tmi, tn_2);
-        tni = 2u * tn_2 + (j & 1u);
+        uint32_t t_m, t_n;
+        group_walk(p.sub256 - 1u + j / Q, tm2, tn2, p.group_m, t_m, t_n);
+        tmi = t_m * QM + (j % Q) / QN;
+        tni = t_n * QN + (j % Q) % QN;
         S = 1u;
-        if ((int64_t)tni * BN >= N)
-            return;  // (the right half of a tile at the right edge that is narrower than 128 + 1 columns)
+        if ((int64_t)tmi * BM >= M || (int64_t)tni * BN >= N)
+            return;  // (a part past the bottom or right edge of a partial tile)
     } else if (p.dp == 0u) {
         tile_split_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, S, p.group_m, tmi, tni, ks);
         stile = tmi * tiles_n + tni;

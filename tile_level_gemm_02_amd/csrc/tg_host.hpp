@@ -193,13 +193,18 @@ inline int64_t split_ws_bytes(int64_t tiles, int splits, int64_t tile_elems)
     return splits <= 1 ? 0 : kSplitCounterBytes + tiles * splits * tile_elems * 4;
 }
 
+// The tiles of a short last round, run without a split in a second launch:
+// each 256 x 256 tile as 2 parts of 256 x 128, 4 of 128 x 128 or 16 of
+// 64 x 64, the smallest parts whose launch fits one round of 256 workgroups.
+enum NtTail : int { kTailNone = 0, kTailWide = 1, kTail128 = 2, kTail64 = 3 };
+
 // Launch plan of the NT kernel: tile edge, LDS ring depth, K split.
 struct NtPlan {
     int tile, nh, splits;
     int64_t ws_bytes;  // workspace the plan needs (0 without a split)
     int64_t dp;        // > 0: this many tiles run whole, the rest split `splits` ways
     int tn;            // the tile's N edge: `tile`, or 128 for the 256 x 128 tile
-    bool tail_wide;    // 256 tile: the first dp tiles whole, then the rest as 256 x 128 halves
+    int tail;          // 256 tile: the first dp tiles whole, then the rest in parts (NtTail)
 };
 
 // Estimated cycles of one compute unit for an NT launch with tile edge T and
@@ -270,8 +275,8 @@ NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
 {
     constexpr int EB = ElemInfo<E>::bytes;
     if (nt_wide<EB, BL>(M, N))  // (one round of its tiles: a K split would not fit the chip)
-        return NtPlan{256, kWideNH, 1, 0, 0, 128, false};
-    NtPlan p{pick_tile_nt<EB>(M, N), 4, 1, 0, 0, 0, false};
+        return NtPlan{256, kWideNH, 1, 0, 0, 128, 0};
+    NtPlan p{pick_tile_nt<EB>(M, N), 4, 1, 0, 0, 0, 0};
     if (EB == 1 && BL == B_NCONTIG && p.tile < 128)
         p.tile = 128;  // (nt_eligible_nrow only admits shapes that pick 128 or 256)
     if (allow_split) {
@@ -323,15 +328,15 @@ NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
             }
         }
     }
-    // A short last round without a split: its tiles run as 256 x 128 column
-    // halves in a second launch (each half about half a tile's time), so the
-    // round takes about half as long; no workspace is needed.
+    // A short last round without a split: its tiles run in parts (NtTail)
+    // in a second launch, which shortens the round; no workspace is needed.
     if (p.tile == 256 && p.splits == 1) {
         const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
         const int64_t D = tiles256 / 256 * 256, R = tiles256 - D;
         if (D > 0 && R > 0 && R * 2 <= 256) {
-            p.tail_wide = true;
             p.dp = D;
+            const bool no64 = EB == 1 && BL == B_NCONTIG;  // (64-byte fp8 B rows: no 64 tile)
+            p.tail = R * 16 <= 256 && !no64 ? kTail64 : R * 4 <= 256 ? kTail128 : kTailWide;
         }
     }
     const int64_t tiles = p.dp > 0 ? ((M + 255) / 256) * ((N + 255) / 256) - p.dp
@@ -379,10 +384,10 @@ tg_status launch_nt_plan(TileArgs& a, const NtPlan& plan, void* ws, hipStream_t 
         a.counters = (uint32_t*)ws;
         a.partials = (float*)((uint8_t*)ws + kSplitCounterBytes);
     }
-    if (plan.tail_wide) {
-        // the first plan.dp tiles of 256 x 256 whole, then every other tile of
-        // the walk as two column halves of 256 x 128, in a second launch
-        const int64_t tiles = n_tiles<256, 256>(a.M, a.N);
+    if (plan.tail != kTailNone) {
+        // the first plan.dp tiles of 256 x 256 whole, then every later tile of
+        // the walk in parts, in a second launch
+        const int64_t rest = n_tiles<256, 256>(a.M, a.N) - plan.dp;
         TileArgs b = a;
         a.dp = (uint32_t)plan.dp;
         tg_status st = plan.nh == 5 ? launch_nt<E, O, 256, 256, BL, 5>(a, 1, s, plan.dp)
@@ -392,7 +397,14 @@ tg_status launch_nt_plan(TileArgs& a, const NtPlan& plan, void* ws, hipStream_t 
         b.dp = 0;
         b.splits = 1;
         b.sub256 = (uint32_t)plan.dp + 1u;
-        return launch_nt<E, O, 256, 128, BL, kWideNH>(b, 1, s, 2 * (tiles - plan.dp));
+        if (plan.tail == kTailWide)
+            return launch_nt<E, O, 256, 128, BL, kWideNH>(b, 1, s, 2 * rest);
+        if (plan.tail == kTail128)
+            return launch_nt<E, O, 128, 128, BL, 8>(b, 1, s, 4 * rest);
+        if constexpr (ElemInfo<E>::bytes == 1 && BL == B_NCONTIG)
+            return TG_ERR_NOT_SUPPORTED;  // (never planned)
+        else
+            return launch_nt<E, O, 64, 64, BL, 8>(b, 1, s, 16 * rest);
     }
     if (plan.tile == 256 && plan.tn == 128) {
         if (plan.nh == 6)

@@ -41,10 +41,11 @@ struct TileArgs {
     // tiles of the walk whole, and only the remaining tiles split K `splits`
     // ways (counters and partial shares are then numbered from tile dp).
     uint32_t dp;
-    // NT kernel with 256 x 128 tiles only: with sub256 > 0, workgroup j
-    // covers column half j % 2 of the 256 x 256 tile at position
-    // sub256 - 1 + j / 2 of the 256 x 256 walk (the tiles that a 256 x 256
-    // launch of the first sub256 - 1 tiles left over).
+    // NT kernel with tiles smaller than 256 x 256 only: with sub256 > 0,
+    // the Q = (256 / BM) x (256 / BN) parts of each 256 x 256 tile of the
+    // 256 x 256 walk from position sub256 - 1 on (the tiles that a 256 x 256
+    // launch of the first sub256 - 1 tiles left over): workgroup j takes
+    // part j % Q (row-major) of tile sub256 - 1 + j / Q.
     uint32_t sub256;
 };
 
