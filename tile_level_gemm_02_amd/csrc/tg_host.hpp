@@ -306,10 +306,15 @@ NtPlan plan_nt(int64_t M, int64_t N, int64_t K, bool allow_split)
         // More than one round of 256 tiles with a short last round: the full
         // rounds run whole tiles and the last round's R tiles split K S ways
         // (R * S <= 256 workgroups, dispatched right behind the whole tiles).
-        if (p.tile == 256 && p.splits == 1) {
+        // Taken for 16-bit inputs with 65 to 128 tiles left over; fewer, and
+        // fp8, run faster as the parts of a second launch (NtTail, below):
+        // bf16 4608^3 (68 left) split 183.3 against parts 189.6 us, but
+        // 6144^3 (64 left) 396.6 against 376.9 and fp8 6144^3 249.6 against
+        // 190.2 (flushed).
+        if (p.tile == 256 && p.splits == 1 && EB == 2) {
             const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
             const int64_t D = tiles256 / 256 * 256, R = tiles256 - D;
-            if (D > 0 && R > 0 && R * 2 <= 256 && R * nt_waves(256) <= kSplitMaxCounters) {
+            if (D > 0 && R > 64 && R * 2 <= 256 && R * nt_waves(256) <= kSplitMaxCounters) {
                 const double whole = (double)(D / 256) * nt_round256_cost(K, EB, 1);
                 const double unsplit = whole + nt_round256_cost(K, EB, 1);
                 double hbest = unsplit;
