@@ -755,9 +755,13 @@ def test_wide_tile_one_hot_exact(tg, dt, lay, shape):
 
 # More than one round of 256 x 256 tiles with a short last round, through
 # the plain entry points: the first 256 tiles of the walk run whole and the
-# rest as 256 x 128 column halves in a second launch.  4300 x 4100: 289
-# tiles, the last round 33 of them, among them the bottom row of tiles (204
-# rows) and the right-edge tiles 4 columns wide (their right halves empty).
+# rest in parts in a second launch — 16 of 64 x 64 for at most 16 tiles left
+# over, 4 of 128 x 128 for at most 64, else 2 of 256 x 128.  4300 x 4100:
+# 289 tiles, 33 left over, among them the bottom row of tiles (204 rows: the
+# lower parts partly or wholly empty) and the right-edge tiles 4 columns
+# wide; 4300 x 4000: 272 tiles, 16 left over (fp8 with row-major B, which has
+# no 64 tile, takes 128 x 128 parts); 4608 x 4608: 324 tiles, 68 left over,
+# halves.
 def _tail_tiles(M, N):
     """(tiles of 256 x 256, tiles of the short last round) (host logic, restated)."""
     t = ((M + 255) // 256) * ((N + 255) // 256)
@@ -766,7 +770,10 @@ def _tail_tiles(M, N):
 
 @pytest.mark.parametrize("dt,lay,out,shape", [
     ("bf16", "col", "bf16", (4300, 4100, 1032)), ("f16", "row", "f32", (4300, 4104, 520)),
-    ("fp8", "col", "bf16", (4300, 4112, 1040)), ("bf16", "col", "f32", (4352, 4352, 272))],
+    ("fp8", "col", "bf16", (4300, 4112, 1040)), ("bf16", "col", "f32", (4352, 4352, 272)),
+    ("bf16", "col", "f32", (4300, 4000, 1032)), ("f16", "row", "f16", (4300, 4000, 520)),
+    ("fp8", "col", "bf16", (4300, 4000, 1040)), ("fp8", "row", "f32", (4300, 4000, 1040)),
+    ("bf16", "row", "bf16", (4608, 4608, 264))],
     ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
 def test_short_last_round_plain(tg, dt, lay, out, shape):
     M, N, K = shape
@@ -778,8 +785,9 @@ def test_short_last_round_plain(tg, dt, lay, out, shape):
 
 
 @pytest.mark.parametrize("dt,lay", [("bf16", "col"), ("fp8", "col"), ("bf16", "row"), ("fp8", "row")])
-def test_short_last_round_plain_one_hot_exact(tg, dt, lay):
-    M, N, K = 4300, 4112, 2064
+@pytest.mark.parametrize("N", [4112, 4000])
+def test_short_last_round_plain_one_hot_exact(tg, dt, lay, N):
+    M, K = 4300, 2064
     assert 0 < _tail_tiles(M, N)[1] <= 128
     Bs = synth.normal((N, K) if lay == "col" else (K, N), 907, std=0.05).to(TDT[dt])
     ks = torch.randint(0, K, (M,), generator=torch.Generator().manual_seed(908))
