@@ -472,7 +472,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt(TileArgs p)
 #pragma unroll
         for (int s = 0; s < KSTEPS - 1; ++s) {
             auto rd = [&](int r) __attribute__((always_inline)) { read_frag(kt, s + 1, (s + 1) & 1, r); };
-            if (s == 0)
+            // (the half-stage freed by the last barrier is copied during the
+            // first sub-step; with an odd ring depth, where that is an A
+            // half-stage, during the second: 1-4% faster at 3072^3 .. 3584^3)
+            if (s == ((NH & 1) && KSTEPS > 2 ? 1 : 0))
                 substep(s & 1, rd,
                         [&](int q) __attribute__((always_inline)) { copy_half(edge, 2 * kt + NH - 1, q, p0, p1); },
                         std::integral_constant<int, ((NH - 1) & 1) ? BI : AI>{});
