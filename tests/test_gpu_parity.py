@@ -66,6 +66,15 @@ def _run_dense(tg, dt, A, B, lay, out, pad=None, scale_a=1.0, scale_b=1.0, C=Non
     return C
 
 
+def _padding_untouched(C):
+    """The columns between N and C's leading dimension keep their NaN fill
+    (the run helpers allocate C with whole 16-byte rows)."""
+    M, N = C.shape
+    ld = C.stride(0)
+    if ld > N and M:
+        assert bool(C.as_strided((M, ld), (ld, 1))[:, N:].isnan().all()), "a padding column of C was written"
+
+
 def _inputs(dt, M, N, K, lay, seed):
     if dt == "fp8":
         A, sa = synth.quantize_e4m3(synth.normal((M, K), seed))
@@ -318,6 +327,7 @@ def test_random_shapes(tg, case):
     dt, lay, out, M, N, K = case
     A, B, sa, sb = _inputs(dt, M, N, K, lay, seed=M * 7 + N * 3 + K)
     C = _run_dense(tg, dt, A, B, lay, out, scale_a=sa, scale_b=sb)
+    _padding_untouched(C)
     _check(C, A, B, dt, lay, out, sa, sb, inner_rel=_fp8_inner(dt, M, N, K, out))
 
 
@@ -955,6 +965,7 @@ def test_random_w4a16_sp24(tg, case):
         cref, S = oracle.gemm_sp24(A, v, m, K)
         ok, r, idx = ochk.check(_f64(C), cref, S, K, out)
     assert ok, (r, idx)
+    _padding_untouched(C)
 
 
 @pytest.mark.parametrize("K", [256, 384, 320])
